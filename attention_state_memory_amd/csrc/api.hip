@@ -1,0 +1,309 @@
+// C ABI of the attention-state-memory library: argument validation,
+// workspace layout and kernel dispatch.  Declarations and the contract of
+// every entry point are in include/asm_memory.h.
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <initializer_list>
+
+#include "asm_memory.h"
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return ASM_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(ASM_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr size_t kAlign = 256;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_dtype(int dtype) {
+  if (dtype != ASM_BF16 && dtype != ASM_F32) return fail(ASM_ERR_DTYPE, "unknown dtype %d", dtype);
+  return ASM_OK;
+}
+
+int check_d(int dtype, int d) {
+  if (d < 1 || d > 256) return fail(ASM_ERR_SHAPE, "head dim d=%d outside 1..256", d);
+  if (dtype == ASM_BF16 && d % 8 != 0)
+    return fail(ASM_ERR_SHAPE, "bf16 head dim d=%d is not a multiple of 8", d);
+  return ASM_OK;
+}
+
+int check_bf16_ptrs(int dtype, std::initializer_list<const void*> ptrs) {
+  if (dtype != ASM_BF16) return ASM_OK;
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return fail(ASM_ERR_ALIGN, "bf16 tensor %p is not 16-byte aligned", p);
+  return ASM_OK;
+}
+
+int check_ws(const void* ws, size_t ws_bytes, size_t need) {
+  if (need == 0) return ASM_OK;
+  if (ws == nullptr) return fail(ASM_ERR_WORKSPACE, "workspace of %zu bytes required, ws is NULL", need);
+  if (ws_bytes < need)
+    return fail(ASM_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, need);
+  if ((reinterpret_cast<uintptr_t>(ws) & 15u) != 0)
+    return fail(ASM_ERR_ALIGN, "workspace %p is not 16-byte aligned", ws);
+  return ASM_OK;
+}
+
+#define ASM_TRY(expr)          \
+  do {                         \
+    const int st_ = (expr);    \
+    if (st_ != ASM_OK) return st_; \
+  } while (0)
+
+// ---- decode planning -------------------------------------------------------
+struct DecodePlan {
+  int split_tok = 0, S_max = 0, score_tiles = 0;
+  size_t off_keys = 0, off_pa = 0, off_pl = 0, total = 0;
+};
+
+int decode_split_tokens(int B, int Hkv, int max_kv_len) {
+  if (const char* e = getenv("ASM_DECODE_SPLIT")) {
+    const int v = atoi(e);
+    if (v >= 32 && v % 32 == 0) return v;
+  }
+  // Aim for about 2048 attention items per step: enough to cover 256 CUs
+  // several times over while keeping the partial-state traffic small.
+  const int64_t work = int64_t(B) * Hkv * max_kv_len;
+  int64_t s = (work + 2047) / 2048;
+  s = (s + 127) / 128 * 128;
+  if (s < 128) s = 128;
+  if (s > 4096) s = 4096;
+  return int(s);
+}
+
+DecodePlan plan_decode(int B, int Hq, int Hkv, int d, int K, int max_kv_len) {
+  DecodePlan p;
+  p.split_tok = decode_split_tokens(B, Hkv, max_kv_len);
+  p.S_max = max_kv_len > 0 ? (max_kv_len + p.split_tok - 1) / p.split_tok : 0;
+  p.score_tiles = (K + 255) / 256;
+  size_t off = 0;
+  p.off_keys = off;
+  off = asmk::align_up(off + size_t(Hq) * p.score_tiles * B * sizeof(uint64_t), kAlign);
+  p.off_pa = off;
+  off = asmk::align_up(off + size_t(B) * Hq * p.S_max * d * sizeof(float), kAlign);
+  p.off_pl = off;
+  off = asmk::align_up(off + size_t(B) * Hq * p.S_max * sizeof(float), kAlign);
+  p.total = off;
+  return p;
+}
+
+int validate_decode_shape(int dtype, int B, int Hq, int Hkv, int d, int K, int max_kv_len) {
+  ASM_TRY(check_dtype(dtype));
+  ASM_TRY(check_d(dtype, d));
+  if (B < 1 || Hq < 1 || Hkv < 1 || K < 1 || max_kv_len < 0)
+    return fail(ASM_ERR_SHAPE, "need B, Hq, Hkv, K >= 1 and max_kv_len >= 0 (B=%d Hq=%d Hkv=%d K=%d max_kv_len=%d)",
+                B, Hq, Hkv, K, max_kv_len);
+  if (Hq % Hkv != 0) return fail(ASM_ERR_SHAPE, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  const int64_t items = int64_t(B) * Hkv * ((int64_t(max_kv_len) + 127) / 128) + int64_t(Hq) * ((K + 255) / 256);
+  if (items > (int64_t(1) << 30) || int64_t(B) * Hq > (int64_t(1) << 30))
+    return fail(ASM_ERR_SHAPE, "decode problem too large for one launch");
+  return ASM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int asm_abi_version(void) { return ASM_ABI_VERSION; }
+
+const char* asm_status_str(int status) {
+  switch (status) {
+    case ASM_OK: return "ok";
+    case ASM_ERR_NULL: return "null pointer";
+    case ASM_ERR_SHAPE: return "unsupported shape";
+    case ASM_ERR_DTYPE: return "unknown dtype";
+    case ASM_ERR_ALIGN: return "misaligned pointer or stride";
+    case ASM_ERR_WORKSPACE: return "workspace missing or too small";
+    case ASM_ERR_HIP: return "HIP launch failure";
+    default: return "unknown status";
+  }
+}
+
+const char* asm_last_error(void) { return g_err; }
+
+// ---------------------------------------------------------------------------
+int asm_centroid_inv_norms(int dtype, int H, int K, int d, const void* C, float* cinv,
+                           hipStream_t stream) {
+  ASM_TRY(check_dtype(dtype));
+  ASM_TRY(check_d(dtype, d));
+  if (H < 0 || K < 0) return fail(ASM_ERR_SHAPE, "negative H or K");
+  if (int64_t(H) * K > (int64_t(1) << 31) - 1) return fail(ASM_ERR_SHAPE, "H*K too large");
+  if (int64_t(H) * K == 0) return ok();
+  if (!C || !cinv) return fail(ASM_ERR_NULL, "C and cinv are required");
+  ASM_TRY(check_bf16_ptrs(dtype, {C}));
+  return hip_status(asmk::launch_inv_norms(dtype, H, K, d, C, cinv, stream), "centroid_inv_norms");
+}
+
+// ---------------------------------------------------------------------------
+size_t asm_decode_step_ws(int dtype, int B, int Hq, int Hkv, int d, int K, int max_kv_len) {
+  if (validate_decode_shape(dtype, B, Hq, Hkv, d, K, max_kv_len) != ASM_OK) return 0;
+  return plan_decode(B, Hq, Hkv, d, K, max_kv_len).total;
+}
+
+int asm_decode_step(int dtype, int B, int Hq, int Hkv, int d, int K, float scale,
+                    const void* q, const void* C, const float* cinv, const float* Abar,
+                    const float* LSEbar, const void* Kl, const void* Vl,
+                    int64_t kv_head_stride, int64_t kv_tok_stride, int64_t kv_capacity,
+                    const int32_t* kv_start, const int32_t* kv_len, int max_kv_len,
+                    float* out, float* out_lse, int32_t* out_idx,
+                    void* ws, size_t ws_bytes, hipStream_t stream) {
+  ASM_TRY(validate_decode_shape(dtype, B, Hq, Hkv, d, K, max_kv_len));
+  if (!(scale == scale) || scale == INFINITY || scale == -INFINITY)
+    return fail(ASM_ERR_SHAPE, "scale must be finite");
+  if (!q || !C || !cinv || !Abar || !LSEbar || !kv_start || !kv_len || !out)
+    return fail(ASM_ERR_NULL, "q, C, cinv, Abar, LSEbar, kv_start, kv_len and out are required");
+  if (max_kv_len > 0) {
+    if (!Kl || !Vl) return fail(ASM_ERR_NULL, "Kl and Vl are required when max_kv_len > 0");
+    if (kv_head_stride < 0 || kv_tok_stride < 1 || kv_capacity < 0)
+      return fail(ASM_ERR_SHAPE, "need kv_head_stride >= 0, kv_tok_stride >= 1, kv_capacity >= 0");
+    if (dtype == ASM_BF16 && (kv_head_stride % 8 != 0 || kv_tok_stride % 8 != 0))
+      return fail(ASM_ERR_ALIGN, "bf16 kv strides must be multiples of 8 elements");
+  }
+  ASM_TRY(check_bf16_ptrs(dtype, {q, C, Kl, Vl}));
+  const DecodePlan p = plan_decode(B, Hq, Hkv, d, K, max_kv_len);
+  ASM_TRY(check_ws(ws, ws_bytes, p.total));
+
+  asmk::DecodeArgs a{};
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.d = d; a.K = K;
+  a.scale2 = scale * ASM_LOG2E;
+  a.q = q; a.C = C; a.cinv = cinv; a.Abar = Abar; a.LSEbar = LSEbar;
+  a.Kl = Kl; a.Vl = Vl;
+  a.kv_head_stride = kv_head_stride; a.kv_tok_stride = kv_tok_stride; a.kv_capacity = kv_capacity;
+  a.kv_start = kv_start; a.kv_len = kv_len; a.max_kv_len = max_kv_len;
+  a.split_tok = p.split_tok; a.S_max = p.S_max; a.score_tiles = p.score_tiles;
+  a.out = out; a.out_lse = out_lse; a.out_idx = out_idx;
+  char* w = static_cast<char*>(ws);
+  a.keys = reinterpret_cast<uint64_t*>(w + p.off_keys);
+  a.part_a = reinterpret_cast<float*>(w + p.off_pa);
+  a.part_lse = reinterpret_cast<float*>(w + p.off_pl);
+  return hip_status(asmk::launch_decode(a, dtype, stream), "decode_step");
+}
+
+// ---------------------------------------------------------------------------
+size_t asm_build_states_ws(int dtype, int Hq, int Hkv, int N, int L, int d, int chunk) {
+  (void)dtype; (void)Hq; (void)Hkv; (void)N; (void)L; (void)d; (void)chunk;
+  return 0;
+}
+
+int asm_build_states(int dtype, int Hq, int Hkv, int N, int L, int d, int chunk, float scale,
+                     const void* Q, const void* Kp, const void* Vp,
+                     float* A_chunks, float* LSE_chunks, float* A, float* LSE, int accumulate,
+                     void* ws, size_t ws_bytes, hipStream_t stream) {
+  (void)ws; (void)ws_bytes;
+  ASM_TRY(check_dtype(dtype));
+  ASM_TRY(check_d(dtype, d));
+  if (Hq < 1 || Hkv < 1 || N < 0 || L < 0 || chunk < 1)
+    return fail(ASM_ERR_SHAPE, "need Hq, Hkv, chunk >= 1 and N, L >= 0");
+  if (Hq % Hkv != 0) return fail(ASM_ERR_SHAPE, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  if (int64_t(Hq) * N > (int64_t(1) << 30)) return fail(ASM_ERR_SHAPE, "Hq*N too large");
+  if (!(scale == scale) || scale == INFINITY || scale == -INFINITY)
+    return fail(ASM_ERR_SHAPE, "scale must be finite");
+  if ((A_chunks == nullptr) != (LSE_chunks == nullptr))
+    return fail(ASM_ERR_NULL, "A_chunks and LSE_chunks must both be given or both be NULL");
+  if (N == 0) return ok();
+  if (!Q || !A || !LSE) return fail(ASM_ERR_NULL, "Q, A and LSE are required");
+  if (L > 0 && (!Kp || !Vp)) return fail(ASM_ERR_NULL, "Kp and Vp are required when L > 0");
+  ASM_TRY(check_bf16_ptrs(dtype, {Q, Kp, Vp}));
+  asmk::StatesArgs a{};
+  a.Hq = Hq; a.Hkv = Hkv; a.N = N; a.L = L; a.d = d; a.chunk = chunk;
+  a.nc = L > 0 ? int((int64_t(L) + chunk - 1) / chunk) : 0;
+  a.scale2 = scale * ASM_LOG2E;
+  a.Q = Q; a.Kp = Kp; a.Vp = Vp;
+  a.A_chunks = A_chunks; a.LSE_chunks = LSE_chunks; a.A = A; a.LSE = LSE;
+  a.accumulate = accumulate ? 1 : 0;
+  return hip_status(asmk::launch_build_states(a, dtype, stream), "build_states");
+}
+
+// ---------------------------------------------------------------------------
+size_t asm_kmeans_assign_ws(int dtype, int H, int N, int K, int d) {
+  (void)dtype; (void)H; (void)N; (void)K; (void)d;
+  return 0;
+}
+
+int asm_kmeans_assign(int dtype, int H, int N, int K, int d, const void* X, const void* C,
+                      const float* cinv, int32_t* idx, float* best,
+                      void* ws, size_t ws_bytes, hipStream_t stream) {
+  (void)ws; (void)ws_bytes;
+  ASM_TRY(check_dtype(dtype));
+  ASM_TRY(check_d(dtype, d));
+  if (H < 0 || N < 0 || K < 1) return fail(ASM_ERR_SHAPE, "need H, N >= 0 and K >= 1");
+  if (int64_t(H) * N > (int64_t(1) << 30) || int64_t(H) * K > (int64_t(1) << 30))
+    return fail(ASM_ERR_SHAPE, "H*N or H*K too large");
+  if (int64_t(H) * N == 0) return ok();
+  if (!X || !C || !cinv || !idx) return fail(ASM_ERR_NULL, "X, C, cinv and idx are required");
+  ASM_TRY(check_bf16_ptrs(dtype, {X, C}));
+  asmk::AssignArgs a{};
+  a.H = H; a.N = N; a.K = K; a.d = d;
+  a.X = X; a.C = C; a.cinv = cinv; a.idx = idx; a.best = best;
+  return hip_status(asmk::launch_assign(a, dtype, stream), "kmeans_assign");
+}
+
+// ---------------------------------------------------------------------------
+static size_t aggregate_ws_bytes(int H, int N, int K) {
+  size_t off = asmk::align_up(size_t(H) * (K + 1) * sizeof(int32_t), kAlign);
+  off += asmk::align_up(size_t(H) * K * sizeof(int32_t), kAlign);
+  off += asmk::align_up(size_t(H) * N * sizeof(int32_t), kAlign);
+  return off;
+}
+
+size_t asm_aggregate_ws(int dtype, int H, int N, int K, int d) {
+  if (check_dtype(dtype) != ASM_OK || check_d(dtype, d) != ASM_OK || H < 0 || N < 0 || K < 1) return 0;
+  return aggregate_ws_bytes(H, N, K);
+}
+
+int asm_aggregate(int dtype, int H, int N, int K, int d, const void* X, const int32_t* idx,
+                  const float* A, const float* LSE, void* C, float* cinv, int32_t* count,
+                  float* Abar, float* LSEbar, void* ws, size_t ws_bytes, hipStream_t stream) {
+  ASM_TRY(check_dtype(dtype));
+  ASM_TRY(check_d(dtype, d));
+  if (H < 0 || N < 0 || K < 1) return fail(ASM_ERR_SHAPE, "need H, N >= 0 and K >= 1");
+  if (int64_t(H) * N > (int64_t(1) << 30) || int64_t(H) * K > (int64_t(1) << 30))
+    return fail(ASM_ERR_SHAPE, "H*N or H*K too large");
+  if (H == 0) return ok();
+  if (!C || !cinv || !count) return fail(ASM_ERR_NULL, "C, cinv and count are required");
+  if (N > 0 && (!X || !idx)) return fail(ASM_ERR_NULL, "X and idx are required when N > 0");
+  if ((Abar == nullptr) != (LSEbar == nullptr))
+    return fail(ASM_ERR_NULL, "Abar and LSEbar must both be given or both be NULL");
+  if (Abar && N > 0 && (!A || !LSE)) return fail(ASM_ERR_NULL, "A and LSE are required with Abar");
+  ASM_TRY(check_bf16_ptrs(dtype, {X, C}));
+  const size_t need = aggregate_ws_bytes(H, N, K);
+  ASM_TRY(check_ws(ws, ws_bytes, need));
+  asmk::AggregateArgs a{};
+  a.H = H; a.N = N; a.K = K; a.d = d;
+  a.X = X; a.idx = idx; a.A = A; a.LSE = LSE; a.C = C; a.cinv = cinv; a.count = count;
+  a.Abar = Abar; a.LSEbar = LSEbar;
+  char* w = static_cast<char*>(ws);
+  size_t off = 0;
+  a.offsets = reinterpret_cast<int32_t*>(w + off);
+  off += asmk::align_up(size_t(H) * (K + 1) * sizeof(int32_t), kAlign);
+  a.cursor = reinterpret_cast<int32_t*>(w + off);
+  off += asmk::align_up(size_t(H) * K * sizeof(int32_t), kAlign);
+  a.perm = reinterpret_cast<int32_t*>(w + off);
+  return hip_status(asmk::launch_aggregate(a, dtype, stream), "aggregate");
+}
+
+}  // extern "C"

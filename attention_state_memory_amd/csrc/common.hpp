@@ -1,0 +1,121 @@
+// Device-side helpers shared by the attention-state-memory kernels (gfx950,
+// wave64).  Nothing here is method-specific arithmetic beyond the packed
+// argmax key and the bf16 unpacking.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <math.h>
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define ASM_LOG2E 1.4426950408889634f
+#define ASM_LN2 0.6931471805599453f
+
+namespace asmk {
+
+constexpr int kWave = 64;
+
+// ---- bf16 / f32 element access -------------------------------------------
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+template <typename T>
+__device__ __forceinline__ float load_elem(const T* p, size_t i);
+template <>
+__device__ __forceinline__ float load_elem<float>(const float* p, size_t i) { return p[i]; }
+template <>
+__device__ __forceinline__ float load_elem<uint16_t>(const uint16_t* p, size_t i) {
+  return __uint_as_float(uint32_t(p[i]) << 16);
+}
+
+// 8 consecutive bf16 (16 bytes, 16-byte aligned) as an MFMA operand.
+__device__ __forceinline__ u32x4 ld16(const uint16_t* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Round a float64 to bf16, nearest with ties to even, in one step (no
+// intermediate float32 rounding).  bf16 keeps 8 significant bits and the
+// float32 exponent range; values whose rounded magnitude reaches 2^128
+// become infinity.
+__device__ __forceinline__ uint16_t f64_to_bf16_rne(double x) {
+  if (isnan(x)) return 0x7FC0;
+  const uint64_t u = __double_as_longlong(x);
+  const uint16_t sign = uint16_t((u >> 48) & 0x8000u);
+  const double ax = fabs(x);
+  if (ax == 0.0) return sign;
+  int e;
+  frexp(ax, &e);                        // ax = m * 2^e, 0.5 <= m < 1
+  int qe = e - 8;                       // spacing of bf16 values near ax
+  if (qe < -133) qe = -133;             // subnormal spacing floor
+  const double q = ldexp(1.0, qe);
+  const double r = rint(ax / q) * q;    // exact division; rint: ties to even
+  if (r >= 0x1p128) return sign | 0x7F80;
+  const uint32_t b32 = __float_as_uint(float(r));  // exact: r has <= 8 significant bits
+  return sign | uint16_t(b32 >> 16);
+}
+
+// ---- argmax keys -----------------------------------------------------------
+// A score s and index k pack into one 64-bit key whose unsigned order is
+// (s ascending, k descending): the maximum key is the highest score, lowest
+// index among exact ties.  -0 is folded into +0 first.
+
+__device__ __forceinline__ uint32_t ordered_bits(float s) {
+  s = s + 0.0f;
+  const uint32_t u = __float_as_uint(s);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ uint64_t argmax_key(float s, uint32_t k) {
+  return (uint64_t(ordered_bits(s)) << 32) | uint64_t(0xFFFFFFFFu - k);
+}
+__device__ __forceinline__ uint32_t key_index(uint64_t key) {
+  return 0xFFFFFFFFu - uint32_t(key & 0xFFFFFFFFull);
+}
+__device__ __forceinline__ float key_score(uint64_t key) {
+  const uint32_t o = uint32_t(key >> 32);
+  const uint32_t u = (o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o;
+  return __uint_as_float(u);
+}
+__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+// ---- wave shuffles -------------------------------------------------------
+
+__device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, kWave); }
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
+  const uint32_t lo = __shfl_xor(uint32_t(v), m, kWave);
+  const uint32_t hi = __shfl_xor(uint32_t(v >> 32), m, kWave);
+  return (uint64_t(hi) << 32) | lo;
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = umax64(v, shfl_xor_u64(v, m));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += shfl_xor_f(v, m);
+  return v;
+}
+__device__ __forceinline__ float readlane_f(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+// Orders LDS traffic between lanes of one wave without a workgroup barrier.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__host__ __device__ constexpr size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace asmk

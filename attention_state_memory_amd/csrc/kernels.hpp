@@ -1,0 +1,93 @@
+// Argument blocks and launchers shared between the HIP kernels and the C ABI
+// layer.  Every launcher enqueues on the given stream and returns the result
+// of hipGetLastError().
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace asmk {
+
+// ---- decode step ----------------------------------------------------------
+struct DecodeArgs {
+  int B, Hq, Hkv, d, K;
+  float scale2;  // softmax scale * log2(e): scores are kept as base-2 logits
+  const void* q;
+  const void* C;
+  const float* cinv;
+  const float* Abar;
+  const float* LSEbar;
+  const void* Kl;
+  const void* Vl;
+  int64_t kv_head_stride, kv_tok_stride, kv_capacity;
+  const int32_t* kv_start;
+  const int32_t* kv_len;
+  int max_kv_len;
+  int split_tok;    // local tokens per attention item
+  int S_max;        // splits per sequence = ceil(max_kv_len / split_tok)
+  int score_tiles;  // ceil(K / 256)
+  float* out;
+  float* out_lse;
+  int32_t* out_idx;
+  uint64_t* keys;   // [Hq, score_tiles, B]
+  float* part_a;    // [B, Hq, S_max, d]
+  float* part_lse;  // [B, Hq, S_max]
+};
+
+bool decode_fast_path(int dtype, int d, int G);
+hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t s);
+
+// ---- centroid inverse norms -------------------------------------------------
+hipError_t launch_inv_norms(int dtype, int H, int K, int d, const void* C, float* cinv,
+                            hipStream_t s);
+
+// ---- prefix states ------------------------------------------------------------
+struct StatesArgs {
+  int Hq, Hkv, N, L, d, chunk, nc;
+  float scale2;
+  const void* Q;
+  const void* Kp;
+  const void* Vp;
+  float* A_chunks;
+  float* LSE_chunks;
+  float* A;
+  float* LSE;
+  int accumulate;
+};
+bool states_fast_path(int dtype, int d, int G);
+hipError_t launch_build_states(const StatesArgs& a, int dtype, hipStream_t s);
+hipError_t launch_states_generic(const StatesArgs& a, int dtype, hipStream_t s);
+
+// ---- k-means assignment -----------------------------------------------------
+struct AssignArgs {
+  int H, N, K, d;
+  const void* X;
+  const void* C;
+  const float* cinv;
+  int32_t* idx;
+  float* best;
+};
+bool assign_fast_path(int dtype, int d);
+hipError_t launch_assign(const AssignArgs& a, int dtype, hipStream_t s);
+hipError_t launch_assign_generic(const AssignArgs& a, int dtype, hipStream_t s);
+
+// ---- aggregation ------------------------------------------------------------
+struct AggregateArgs {
+  int H, N, K, d;
+  const void* X;
+  const int32_t* idx;
+  const float* A;
+  const float* LSE;
+  void* C;
+  float* cinv;
+  int32_t* count;
+  float* Abar;
+  float* LSEbar;
+  int32_t* offsets;  // [H, K+1] workspace
+  int32_t* cursor;   // [H, K]   workspace
+  int32_t* perm;     // [H, N]   workspace
+};
+hipError_t launch_aggregate(const AggregateArgs& a, int dtype, hipStream_t s);
+
+}  // namespace asmk

@@ -1,0 +1,372 @@
+// Offline memory build of attention-state memory on gfx950: the aggregation
+// step, centroid inverse norms, and the plain VALU kernels for k-means
+// assignment and prefix states (float32 data and shapes outside the MFMA
+// kernels).
+//
+// Source: "Context Memorization for Efficient Long Context Generation"
+// (technical summary), Fase de Calibración Offline -- Recolección (per query,
+// the attention state over the prefix), Agrupamiento (cluster the queries),
+// Agregación (centroid = mean of the cluster's queries; the entry's state
+// merges the members' states with the online-softmax rule), Eficiencia (a
+// long prefix is processed in chunks merged by the same identity).
+//
+// Aggregation is a counting sort of the queries by cluster followed by one
+// wave per cluster:
+//   fill(count) -> histogram(count) -> per-head exclusive scan (offsets,
+//   cursor) -> scatter (perm) -> finalize (mean, cinv, Z-weighted state).
+// Sums run in float64: a bf16 mean is then the float64 mean rounded once to
+// bf16, and the member order inside a cluster (set by atomics) does not
+// change the result unless a float64 sum is inexact.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace asmk {
+
+// ---------------------------------------------------------------------------
+// inverse norms
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ void __launch_bounds__(256) inv_norms_kernel(int HK, int d, const T* C, float* cinv) {
+  const int lane = threadIdx.x & 63;
+  const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (item >= HK) return;
+  double ss = 0.0;
+  for (int x = lane; x < d; x += 64) {
+    const double c = load_elem(C, size_t(item) * d + x);
+    ss = fma(c, c, ss);
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
+  if (lane == 0) cinv[item] = ss > 0.0 ? float(1.0 / sqrt(ss)) : 0.0f;
+}
+
+hipError_t launch_inv_norms(int dtype, int H, int K, int d, const void* C, float* cinv,
+                            hipStream_t s) {
+  const int HK = H * K;
+  if (HK == 0) return hipSuccess;
+  const dim3 grid((HK + 3) / 4);
+  if (dtype == 1)
+    hipLaunchKernelGGL(inv_norms_kernel<float>, grid, dim3(256), 0, s, HK, d,
+                       static_cast<const float*>(C), cinv);
+  else
+    hipLaunchKernelGGL(inv_norms_kernel<uint16_t>, grid, dim3(256), 0, s, HK, d,
+                       static_cast<const uint16_t*>(C), cinv);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// aggregation
+// ---------------------------------------------------------------------------
+__global__ void fill_i32(int32_t* p, int64_t n, int32_t v) {
+  for (int64_t i = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; i < n;
+       i += int64_t(gridDim.x) * blockDim.x)
+    p[i] = v;
+}
+
+__global__ void agg_histogram(AggregateArgs a) {
+  const int64_t total = int64_t(a.H) * a.N;
+  for (int64_t t = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; t < total;
+       t += int64_t(gridDim.x) * blockDim.x) {
+    const int h = int(t / a.N);
+    const int k = a.idx[t];
+    if (k >= 0 && k < a.K) atomicAdd(&a.count[size_t(h) * a.K + k], 1);
+  }
+}
+
+// One 1024-thread workgroup per head: exclusive scan of count[h, :].
+__global__ void __launch_bounds__(1024) agg_scan(AggregateArgs a) {
+  __shared__ int32_t wsum[16];
+  __shared__ int32_t carry_s;
+  const int h = blockIdx.x;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int32_t* cnt = a.count + size_t(h) * a.K;
+  int32_t* off = a.offsets + size_t(h) * (a.K + 1);
+  int32_t* cur = a.cursor + size_t(h) * a.K;
+  if (t == 0) carry_s = 0;
+  __syncthreads();
+  for (int base = 0; base < a.K; base += 1024) {
+    const int k = base + t;
+    const int32_t v = k < a.K ? cnt[k] : 0;
+    int32_t x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int32_t y = __shfl_up(x, o, 64);
+      if (lane >= o) x += y;
+    }
+    if (lane == 63) wsum[w] = x;
+    __syncthreads();
+    int32_t before = carry_s;
+    for (int ww = 0; ww < w; ++ww) before += wsum[ww];
+    const int32_t excl = before + x - v;
+    if (k < a.K) {
+      off[k] = excl;
+      cur[k] = excl;
+    }
+    __syncthreads();
+    if (t == 1023) carry_s = excl + v;
+    __syncthreads();
+  }
+  if (t == 0) off[a.K] = carry_s;
+}
+
+__global__ void agg_scatter(AggregateArgs a) {
+  const int64_t total = int64_t(a.H) * a.N;
+  for (int64_t t = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; t < total;
+       t += int64_t(gridDim.x) * blockDim.x) {
+    const int h = int(t / a.N);
+    const int i = int(t - int64_t(h) * a.N);
+    const int k = a.idx[t];
+    if (k >= 0 && k < a.K) {
+      const int pos = atomicAdd(&a.cursor[size_t(h) * a.K + k], 1);
+      a.perm[size_t(h) * a.N + pos] = i;
+    }
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void store_rounded(T* p, size_t i, double v);
+template <>
+__device__ __forceinline__ void store_rounded<float>(float* p, size_t i, double v) {
+  p[i] = float(v);
+}
+template <>
+__device__ __forceinline__ void store_rounded<uint16_t>(uint16_t* p, size_t i, double v) {
+  p[i] = f64_to_bf16_rne(v);
+}
+
+// One wave per (head, cluster).  d <= 256: lane owns dims lane + 64*j.
+template <typename T>
+__global__ void __launch_bounds__(256) agg_finalize(AggregateArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (item >= a.H * a.K) return;
+  const int h = item / a.K, k = item % a.K;
+  const int d = a.d;
+  const int32_t* off = a.offsets + size_t(h) * (a.K + 1);
+  const int beg = off[k];
+  const int n = off[k + 1] - beg;
+  const int32_t* mem = a.perm + size_t(h) * a.N + beg;
+  T* Crow = static_cast<T*>(a.C) + size_t(item) * d;
+  const T* X = static_cast<const T*>(a.X) + size_t(h) * a.N * d;
+
+  double cval[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int x = lane + 64 * j;
+    cval[j] = x < d ? double(load_elem(Crow, x)) : 0.0;
+  }
+  if (n > 0) {
+    double sum[4] = {0.0, 0.0, 0.0, 0.0};
+    for (int m = 0; m < n; ++m) {
+      const size_t row = size_t(mem[m]) * d;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int x = lane + 64 * j;
+        if (x < d) sum[j] += double(load_elem(X, row + x));
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int x = lane + 64 * j;
+      if (x < d) {
+        store_rounded<T>(Crow, x, sum[j] / double(n));
+        cval[j] = double(load_elem(Crow, x));
+      }
+    }
+  }
+  double ss = 0.0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) ss = fma(cval[j], cval[j], ss);
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
+  if (lane == 0) a.cinv[item] = ss > 0.0 ? float(1.0 / sqrt(ss)) : 0.0f;
+
+  if (a.Abar == nullptr) return;
+  float* ab = a.Abar + size_t(item) * d;
+  const float* LSE = a.LSE + size_t(h) * a.N;
+  const float* A = a.A + size_t(h) * a.N * d;
+  float mx = -INFINITY;
+  for (int m = lane; m < n; m += 64) mx = fmaxf(mx, LSE[mem[m]]);
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) mx = fmaxf(mx, __shfl_xor(mx, m, 64));
+  if (n == 0 || mx == -INFINITY) {
+    for (int x = lane; x < d; x += 64) ab[x] = 0.0f;
+    if (lane == 0) a.LSEbar[item] = -INFINITY;
+    return;
+  }
+  double z = 0.0, acc[4] = {0.0, 0.0, 0.0, 0.0};
+  for (int m = 0; m < n; ++m) {
+    const int i = mem[m];
+    const float li = LSE[i];
+    if (li == -INFINITY) continue;
+    const double wgt = exp(double(li) - double(mx));
+    z += wgt;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int x = lane + 64 * j;
+      if (x < d) acc[j] = fma(wgt, double(A[size_t(i) * d + x]), acc[j]);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int x = lane + 64 * j;
+    if (x < d) ab[x] = float(acc[j] / z);
+  }
+  if (lane == 0) a.LSEbar[item] = float(double(mx) + log(z) - log(double(n)));
+}
+
+hipError_t launch_aggregate(const AggregateArgs& a, int dtype, hipStream_t s) {
+  const int64_t HK = int64_t(a.H) * a.K, HN = int64_t(a.H) * a.N;
+  if (HK == 0) return hipSuccess;
+  auto grid_for = [](int64_t n) { return dim3(unsigned((n + 255) / 256 < 65536 ? (n + 255) / 256 : 65536)); };
+  hipLaunchKernelGGL(fill_i32, grid_for(HK), dim3(256), 0, s, a.count, HK, 0);
+  if (HN > 0) hipLaunchKernelGGL(agg_histogram, grid_for(HN), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(agg_scan, dim3(a.H), dim3(1024), 0, s, a);
+  if (HN > 0) hipLaunchKernelGGL(agg_scatter, grid_for(HN), dim3(256), 0, s, a);
+  const dim3 fgrid(unsigned((HK + 3) / 4));
+  if (dtype == 1)
+    hipLaunchKernelGGL(agg_finalize<float>, fgrid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(agg_finalize<uint16_t>, fgrid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// plain VALU k-means assignment: one wave per query
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ void __launch_bounds__(256) assign_generic(AssignArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (item >= a.H * a.N) return;
+  const int h = item / a.N;
+  const int d = a.d;
+  const T* X = static_cast<const T*>(a.X);
+  const T* C = static_cast<const T*>(a.C) + size_t(h) * a.K * d;
+  const float* ci = a.cinv + size_t(h) * a.K;
+  float qv[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int x = lane + 64 * j;
+    qv[j] = x < d ? load_elem(X, size_t(item) * d + x) : 0.0f;
+  }
+  uint64_t best = 0;
+  for (int k = 0; k < a.K; ++k) {
+    float s = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int x = lane + 64 * j;
+      if (x < d) s = fmaf(qv[j], load_elem(C, size_t(k) * d + x), s);
+    }
+    s = wave_sum(s);
+    best = umax64(best, argmax_key(s * ci[k], uint32_t(k)));
+  }
+  if (lane == 0) {
+    a.idx[item] = int32_t(key_index(best));
+    if (a.best) a.best[item] = key_score(best);
+  }
+}
+
+hipError_t launch_assign_generic(const AssignArgs& a, int dtype, hipStream_t s) {
+  const int64_t HN = int64_t(a.H) * a.N;
+  if (HN == 0) return hipSuccess;
+  const dim3 grid(unsigned((HN + 3) / 4));
+  if (dtype == 1)
+    hipLaunchKernelGGL(assign_generic<float>, grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(assign_generic<uint16_t>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// plain VALU prefix states: one wave per (query head, query)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void merge_state(float& l1, float* a1, float l2, const float* a2) {
+  const float M = fmaxf(l1, l2);
+  if (M == -INFINITY) return;
+  const float w1 = l1 == -INFINITY ? 0.0f : expf(l1 - M);
+  const float w2 = l2 == -INFINITY ? 0.0f : expf(l2 - M);
+  const float z = w1 + w2;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) a1[j] = (w1 * a1[j] + w2 * a2[j]) / z;
+  l1 = M + logf(z);
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256) states_generic(StatesArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (item >= a.Hq * a.N) return;
+  const int h = item / a.N;
+  const int g = h / (a.Hq / a.Hkv);
+  const int d = a.d;
+  const T* Q = static_cast<const T*>(a.Q);
+  const T* Kg = static_cast<const T*>(a.Kp) + size_t(g) * a.L * d;
+  const T* Vg = static_cast<const T*>(a.Vp) + size_t(g) * a.L * d;
+  float qv[4], ra[4];
+  float rl = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int x = lane + 64 * j;
+    qv[j] = x < d ? load_elem(Q, size_t(item) * d + x) : 0.0f;
+    ra[j] = (a.accumulate && x < d) ? a.A[size_t(item) * d + x] : 0.0f;
+  }
+  if (a.accumulate) rl = a.LSE[item];
+  for (int c = 0; c < a.nc; ++c) {
+    const int lo = c * a.chunk, hi = min(a.L, lo + a.chunk);
+    float m = -INFINITY, l = 0.0f, acc[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int t = lo; t < hi; ++t) {
+      float s = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int x = lane + 64 * j;
+        if (x < d) s = fmaf(qv[j], load_elem(Kg, size_t(t) * d + x), s);
+      }
+      s = wave_sum(s) * a.scale2;
+      const float mn = fmaxf(m, s);
+      const float al = __builtin_amdgcn_exp2f(m - mn);
+      const float p = __builtin_amdgcn_exp2f(s - mn);
+      l = l * al + p;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int x = lane + 64 * j;
+        const float v = x < d ? load_elem(Vg, size_t(t) * d + x) : 0.0f;
+        acc[j] = fmaf(p, v, acc[j] * al);
+      }
+      m = mn;
+    }
+    float ca[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ca[j] = acc[j] / l;
+    const float cl = (m + log2f(l)) * ASM_LN2;
+    if (a.A_chunks) {
+      const size_t row = size_t(c) * a.Hq * a.N + item;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int x = lane + 64 * j;
+        if (x < d) a.A_chunks[row * d + x] = ca[j];
+      }
+      if (lane == 0) a.LSE_chunks[row] = cl;
+    }
+    merge_state(rl, ra, cl, ca);
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int x = lane + 64 * j;
+    if (x < d) a.A[size_t(item) * d + x] = rl == -INFINITY ? 0.0f : ra[j];
+  }
+  if (lane == 0) a.LSE[item] = rl;
+}
+
+hipError_t launch_states_generic(const StatesArgs& a, int dtype, hipStream_t s) {
+  const int64_t HN = int64_t(a.Hq) * a.N;
+  if (HN == 0) return hipSuccess;
+  const dim3 grid(unsigned((HN + 3) / 4));
+  if (dtype == 1)
+    hipLaunchKernelGGL(states_generic<float>, grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(states_generic<uint16_t>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace asmk

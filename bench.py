@@ -1,0 +1,212 @@
+"""Benchmark: attention-state-memory decode at K=8192 on one MI355X.
+
+Workload (synthetic, seeded): LLaMA-3.1-8B attention-head shapes (32 query
+heads, 8 kv heads, d=128), K=8192 memory entries per query head, batch 32
+with ragged local contexts uniform in [512, 4096]; bf16 q/C/K/V, float32
+states.  A step is one asm_decode_step call -- centroid scoring, argmax,
+state gather, split-K local attention and the online-softmax merge -- over
+one batch.  R replicas of the inputs are resident in HBM and rotated so the
+256 MB last-level cache does not hold a step's working set.
+
+Prints one JSON line: whole-job head-queries/s, ms/step, the roofline of the
+fused decode kernel (algorithmic bytes / kernel time vs 8 TB/s), and the fp64
+CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def algorithmic_bytes(inp) -> int:
+    """Bytes a decode step must move: the centroid table and its inverse
+    norms, the gathered states, the local KV of every sequence, the queries
+    and the outputs (out, lse, idx).  The prefix is never read."""
+    B, Hq, Hkv, d, K = inp["B"], inp["Hq"], inp["Hkv"], inp["d"], inp["K"]
+    e = 2 if inp["dtype"] == "bf16" else 4
+    table = Hq * K * d * e + Hq * K * 4
+    gathered = B * Hq * (d * 4 + 4)
+    kv = int(np.sum(inp["kv_len"])) * Hkv * d * e * 2
+    q = B * Hq * d * e
+    outs = B * Hq * (d * 4 + 4 + 4)
+    lens = B * 8
+    return table + gathered + kv + q + outs + lens
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--replicas", type=int, default=4)
+    p.add_argument("--no-graph", action="store_true", help="launch eagerly instead of a HIP graph")
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="wall-clock budget of the CPU oracle baseline (0 disables it)")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; "
+                                   "multi-GPU runs are not part of this build"}))
+        sys.exit(2)
+    import torch
+    from attention_state_memory_amd import api, synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def to_dev(x):
+        x = np.ascontiguousarray(x)
+        if x.dtype == np.uint16:
+            return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(x).to(dev)
+
+    reps, host_inputs = [], []
+    for r in range(args.replicas):
+        inp = synth.batched_decode(r)
+        host_inputs.append(inp)
+        t = {k: to_dev(inp[k]) for k in ("q", "C", "Abar", "LSEbar", "Kl", "Vl", "kv_start", "kv_len")}
+        t["cinv"] = api.centroid_inv_norms(t["C"])
+        t["max_kv_len"] = int(np.max(inp["kv_len"]))
+        reps.append(t)
+        print(f"replica {r} resident", file=sys.stderr, flush=True)
+    inp0 = host_inputs[0]
+    B, Hq, Hkv, d, K = inp0["B"], inp0["Hq"], inp0["Hkv"], inp0["d"], inp0["K"]
+    max_kv = 4096
+    code = api.BF16
+    ws_bytes = api.decode_step_ws(code, B, Hq, Hkv, d, K, max_kv)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+    out_lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    out_idx = torch.empty((B, Hq), dtype=torch.int32, device=dev)
+    L = api.lib()
+    P = ctypes.c_void_p
+
+    def make_call(t, stream):
+        cap = t["Kl"].shape[1]
+        argv = (code, B, Hq, Hkv, d, K, ctypes.c_float(inp0["scale"]), P(t["q"].data_ptr()),
+                P(t["C"].data_ptr()), P(t["cinv"].data_ptr()), P(t["Abar"].data_ptr()),
+                P(t["LSEbar"].data_ptr()), P(t["Kl"].data_ptr()), P(t["Vl"].data_ptr()),
+                t["Kl"].stride(0), t["Kl"].stride(1), cap, P(t["kv_start"].data_ptr()),
+                P(t["kv_len"].data_ptr()), max_kv, P(out.data_ptr()), P(out_lse.data_ptr()),
+                P(out_idx.data_ptr()), P(ws.data_ptr()), ws_bytes, P(stream))
+
+        def call():
+            st = L.asm_decode_step(*argv)
+            if st != 0:
+                raise RuntimeError(L.asm_last_error().decode())
+        return call
+
+    stream = torch.cuda.Stream(dev)
+    calls = [make_call(t, stream.cuda_stream) for t in reps]
+    R = len(calls)
+
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            calls[i % R]()
+    stream.synchronize()
+
+    graph = None
+    if not args.no_graph:
+        # one graph holds one pass over the R replicas
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            for c in calls:
+                c()
+        with torch.cuda.stream(stream):
+            graph.replay()
+        stream.synchronize()
+
+    steps = args.steps if graph is None else max(R, (args.steps // R) * R)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        if graph is None:
+            for i in range(steps):
+                calls[i % R]()
+        else:
+            for _ in range(steps // R):
+                graph.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms_total = e0.elapsed_time(e1)
+    ms_step = ms_total / steps
+    queries = B * Hq
+    qps = queries / (ms_step * 1e-3)
+    alg_bytes = float(np.mean([algorithmic_bytes(h) for h in host_inputs]))
+    achieved = alg_bytes / (ms_step * 1e-3) / 1e9
+
+    result = {
+        "metric": "ASM decode queries/sec (heads x tokens) at K=8192; achieved HBM GB/s vs peak",
+        "value": qps,
+        "unit": "head-queries/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 q/C/K/V, fp32 states, lse~U(5,12))",
+        "config": {"workload": "batched_decode", "K": K, "batch": B, "q_heads": Hq,
+                   "kv_heads": Hkv, "head_dim": d, "local_len": "U{512..4096}",
+                   "replicas": R, "launch": "eager" if graph is None else "hip_graph"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "algorithmic_bytes_per_step": alg_bytes,
+                     "timed": "whole decode step (fused main kernel + combine kernel)"},
+    }
+
+    # ---- CPU baseline: the fp64 oracle, bounded sample of the same workload
+    if args.cpu_seconds > 0:
+        result["cpu_baseline"] = cpu_baseline(inp0, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(inp, budget_s: float) -> dict:
+    from threadpoolctl import threadpool_info
+    from oracle import asm_oracle as O
+    q64 = O.bf16_bits_to_f64(inp["q"])
+    C64 = O.bf16_bits_to_f64(inp["C"])
+    Ab = inp["Abar"].astype(np.float64)
+    Lb = inp["LSEbar"].astype(np.float64)
+    Kl = O.bf16_bits_to_f64(inp["Kl"])
+    Vl = O.bf16_bits_to_f64(inp["Vl"])
+    B = inp["B"]
+    ks = [Kl[:, s:s + n] for s, n in zip(inp["kv_start"], inp["kv_len"])]
+    vs = [Vl[:, s:s + n] for s, n in zip(inp["kv_start"], inp["kv_len"])]
+    # sample: whole decode steps over replica 0 (all 32 sequences x 32 heads),
+    # repeated until the wall-clock budget is spent (at least one step)
+    t0 = time.perf_counter()
+    passes = 0
+    while passes == 0 or (time.perf_counter() - t0) < budget_s:
+        O.decode(q64, C64, Ab, Lb, ks, vs, inp["scale"])
+        passes += 1
+    el = time.perf_counter() - t0
+    done = passes * B
+    threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    return {"value": done * inp["Hq"] / el, "unit": "head-queries/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{passes} full decode step(s) of replica 0 ({B} sequences x "
+                      f"{inp['Hq']} heads, K={inp['K']} scoring + local attention), {el:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,184 @@
+/*
+ * attention-state memory (ASM) on MI355X (gfx950): the library's C ABI.
+ *
+ * The method (sources cited by page title and section):
+ *   [TS]   "Context Memorization for Efficient Long Context Generation",
+ *          technical summary (gist.science): Metodología; Fase de
+ *          Calibración Offline (Recolección, Agrupamiento, Agregación,
+ *          Eficiencia); Fase de Inferencia Online (Recuperación, Fusión).
+ *   [NEWS] "Búsqueda de Memoria Reemplaza Atención Lineal en Prefijos
+ *          Largos" (aiexpert.news), the paragraph on how the method works.
+ *
+ * A long fixed prefix is replaced by a table of K entries per query head.
+ * Entry k holds a centroid query c_k and the attention state (a_k, lse_k)
+ * that summarises attention over the prefix: a is the softmax-weighted mean
+ * of the values and lse = log Z, Z = sum_j exp(scale * q.k_j) ([TS]
+ * Metodología).  The empty state is (a = 0, lse = -inf).
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers, row-major, densely packed in
+ *     the layout given (the local KV of asm_decode_step takes strides).
+ *     Shapes and scalars are host values.
+ *   - dtype selects the element type of the "void*" tensors: ASM_BF16
+ *     (uint16 bf16 bit patterns) or ASM_F32.  States (a, lse), inverse
+ *     norms and outputs are always float32.
+ *   - The caller owns every buffer, including the workspace `ws` whose size
+ *     the matching *_ws() function returns (0 means ws may be NULL).  The
+ *     library allocates no memory and keeps no state between calls except a
+ *     thread-local error message.
+ *   - Calls validate their arguments on the host before any launch, enqueue
+ *     their kernels on `stream` and return without synchronising.  A
+ *     negative status means nothing was enqueued (or, for ASM_ERR_HIP, that
+ *     a launch failed); asm_last_error() then describes the problem.  Faults
+ *     inside kernels surface at the caller's next synchronisation.
+ *   - bf16 tensors must be 16-byte aligned; every row length and stride
+ *     counted in elements must be a multiple of 8.
+ *   - Outputs must not overlap inputs unless an entry point says so.
+ *   - Two calls that share a workspace must not run concurrently.
+ */
+#ifndef ASM_MEMORY_H
+#define ASM_MEMORY_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum asm_status_code {
+  ASM_OK = 0,
+  ASM_ERR_NULL = -1,      /* a required pointer is NULL */
+  ASM_ERR_SHAPE = -2,     /* a shape or scalar is out of the supported range */
+  ASM_ERR_DTYPE = -3,     /* unknown dtype */
+  ASM_ERR_ALIGN = -4,     /* pointer or stride misaligned for bf16 vector loads */
+  ASM_ERR_WORKSPACE = -5, /* ws_bytes smaller than the *_ws() size, or ws NULL */
+  ASM_ERR_HIP = -6        /* a HIP launch failed; see asm_last_error() */
+};
+
+enum asm_dtype { ASM_BF16 = 0, ASM_F32 = 1 };
+
+/* ABI version of this header (bumped on any signature change). */
+#define ASM_ABI_VERSION 1
+int asm_abi_version(void);
+
+/* Static text for a status code. */
+const char* asm_status_str(int status);
+
+/* Thread-local description of the last failure on this thread ("" if none). */
+const char* asm_last_error(void);
+
+/*
+ * asm_centroid_inv_norms -- cinv[h,k] = 1/|C[h,k,:]|, or 0 for a zero row.
+ * Retrieval scores a query against centroid k by cosine similarity ([TS]
+ * Recuperación); the kernels use q.c_k * cinv_k, which orders centroids as
+ * the cosine does for a fixed query.
+ *   C    [H, K, d] dtype;  cinv [H, K] float32 (output).
+ *   1 <= d <= 256 (multiple of 8 for bf16); H, K >= 0.
+ */
+int asm_centroid_inv_norms(int dtype, int H, int K, int d, const void* C, float* cinv,
+                           hipStream_t stream);
+
+/*
+ * asm_decode_step -- one decode step against the memory ([TS] Recuperación
+ * and Fusión; [NEWS]).  For every sequence b and query head h:
+ *   1. idx[b,h] = the k maximising q[b,h].C[h,k] * cinv[h,k] (the cosine
+ *      order), the lowest such k on exact float32 ties;
+ *   2. the memory state (Abar[h,idx], LSEbar[h,idx]) is gathered;
+ *   3. the local state: attention of q[b,h] over the sequence's local
+ *      (non-prefix) tokens t = 0..kv_len[b]-1 of kv head g = h / (Hq/Hkv),
+ *      with scores scale * q.k_t;
+ *   4. out, out_lse = the online-softmax merge of the two states:
+ *      a = (Z1 a1 + Z2 a2)/(Z1 + Z2), lse = log(Z1 + Z2).
+ *   Prefix tokens are never read.
+ * Arguments:
+ *   B >= 1 sequences; Hq query heads, Hkv kv heads, Hq % Hkv == 0;
+ *   d in {64, 128} for bf16 (any 1..256 for float32); K >= 1 entries.
+ *   q      [B, Hq, d] dtype
+ *   C      [Hq, K, d] dtype          cinv [Hq, K] float32 (see above)
+ *   Abar   [Hq, K, d] float32        LSEbar [Hq, K] float32 (-inf = empty)
+ *   Kl, Vl dtype; local key/value of (kv head g, token slot p) starts at
+ *          element g*kv_head_stride + p*kv_tok_stride, d contiguous values.
+ *          Sequence b occupies slots kv_start[b] .. kv_start[b]+kv_len[b]-1.
+ *   kv_capacity  number of token slots addressable per kv head.
+ *   kv_start, kv_len  [B] int32, device memory.
+ *   max_kv_len   host-side upper bound on every kv_len[b] (sizes the grid).
+ *   out    [B, Hq, d] float32; out_lse [B, Hq] float32 (nullable);
+ *   out_idx [B, Hq] int32 (nullable).
+ * A sequence whose kv_len/kv_start is negative, exceeds max_kv_len or runs
+ * past kv_capacity is not read: its outputs are NaN (idx still written).
+ * kv_len[b] == 0 gives the memory state itself.
+ */
+size_t asm_decode_step_ws(int dtype, int B, int Hq, int Hkv, int d, int K, int max_kv_len);
+int asm_decode_step(int dtype, int B, int Hq, int Hkv, int d, int K, float scale,
+                    const void* q, const void* C, const float* cinv, const float* Abar,
+                    const float* LSEbar, const void* Kl, const void* Vl,
+                    int64_t kv_head_stride, int64_t kv_tok_stride, int64_t kv_capacity,
+                    const int32_t* kv_start, const int32_t* kv_len, int max_kv_len,
+                    float* out, float* out_lse, int32_t* out_idx,
+                    void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * asm_build_states -- prefix attention states of the calibration queries
+ * ([TS] Recolección), chunk by chunk ([TS] Eficiencia: the prefix may be cut
+ * into chunks encoded independently and merged with the online-softmax
+ * identity).  For query head h (kv head g = h / (Hq/Hkv)) and query i:
+ *   chunk c covers prefix tokens [c*chunk, min(L, (c+1)*chunk));
+ *   (a_c, lse_c) = attention state of Q[h,i] over that chunk;
+ *   the merged state is the running merge over c = 0, 1, ... in order.
+ * Arguments:
+ *   Q [Hq, N, d] dtype; Kp, Vp [Hkv, L, d] dtype; chunk >= 1.
+ *   A_chunks [nc, Hq, N, d], LSE_chunks [nc, Hq, N] float32, nullable
+ *     (nc = ceil(L/chunk)): per-chunk states, written when non-NULL.
+ *   A [Hq, N, d], LSE [Hq, N] float32: merged states.  With accumulate != 0
+ *     the incoming (A, LSE) are merged with this call's prefix states (a
+ *     prefix streamed in pieces); otherwise they are overwritten.
+ *   d in {64, 128} for bf16 (any 1..256 for float32).
+ *   bf16 builds take the value products in fp16 (see the design notes):
+ *   |Vp| must stay below 65504.
+ */
+size_t asm_build_states_ws(int dtype, int Hq, int Hkv, int N, int L, int d, int chunk);
+int asm_build_states(int dtype, int Hq, int Hkv, int N, int L, int d, int chunk, float scale,
+                     const void* Q, const void* Kp, const void* Vp,
+                     float* A_chunks, float* LSE_chunks, float* A, float* LSE, int accumulate,
+                     void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * asm_kmeans_assign -- nearest centroid by cosine for every collected query
+ * ([TS] Agrupamiento clusters the queries; the metric is the retrieval
+ * cosine of [TS] Recuperación).
+ *   idx[h,i] = argmax_k X[h,i,:].C[h,k,:] * cinv[h,k], lowest k on ties.
+ *   X [H, N, d] dtype; C [H, K, d] dtype; cinv [H, K] float32;
+ *   idx [H, N] int32; best [H, N] float32 (nullable): the winning
+ *   X.C * cinv (cosine times |x|).
+ */
+size_t asm_kmeans_assign_ws(int dtype, int H, int N, int K, int d);
+int asm_kmeans_assign(int dtype, int H, int N, int K, int d, const void* X, const void* C,
+                      const float* cinv, int32_t* idx, float* best,
+                      void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * asm_aggregate -- one memory-table update from an assignment ([TS]
+ * Agregación).  Per head h and cluster k with members M = {i : idx[h,i]=k},
+ * n = |M|:
+ *   count[h,k] = n;
+ *   n > 0: C[h,k] = mean of X[h,i] over M, summed in float64 and rounded
+ *          once (nearest-even) to dtype;  n == 0: C[h,k] unchanged;
+ *   cinv[h,k] = 1/|C[h,k]| (0 for a zero row), after the update;
+ *   if Abar/LSEbar are non-NULL (then A and LSE must be too):
+ *     Abar[h,k] = sum_M Z_i A[h,i] / sum_M Z_i,  Z_i = exp(LSE[h,i]),
+ *     LSEbar[h,k] = log(mean_M Z_i);  (0, -inf) for an empty cluster.
+ *   X [H, N, d] dtype; idx [H, N] int32 with 0 <= idx < K (others ignored);
+ *   A [H, N, d], LSE [H, N] float32; C [H, K, d] dtype (in/out);
+ *   cinv [H, K] float32; count [H, K] int32; Abar [H, K, d], LSEbar [H, K].
+ */
+size_t asm_aggregate_ws(int dtype, int H, int N, int K, int d);
+int asm_aggregate(int dtype, int H, int N, int K, int d, const void* X, const int32_t* idx,
+                  const float* A, const float* LSE, void* C, float* cinv, int32_t* count,
+                  float* Abar, float* LSEbar, void* ws, size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ASM_MEMORY_H */

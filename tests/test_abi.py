@@ -1,0 +1,124 @@
+"""CPU checks of the C ABI: the library loads, exports every function that
+include/asm_memory.h declares, and rejects bad arguments on the host before
+touching the GPU (no compute calls here)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from attention_state_memory_amd import api
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "asm_memory.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(asm_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ["asm_build_states", "asm_kmeans_assign", "asm_aggregate", "asm_decode_step",
+              "asm_centroid_inv_norms", "asm_abi_version", "asm_status_str", "asm_last_error"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = api.lib()
+    names = declared_functions()
+    for n in names:
+        assert hasattr(L, n), f"{n} not exported"
+    assert set(names) == set(api.SIGNATURES), "binding signatures differ from the header"
+    out = subprocess.run(["nm", "-D", "--defined-only", api.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (asm_\w+)$", out, flags=re.M))
+    assert set(names) <= exported
+
+
+def test_abi_version_and_status_text():
+    L = api.lib()
+    assert L.asm_abi_version() == 1
+    text = open(HEADER).read()
+    assert int(re.search(r"#define ASM_ABI_VERSION (\d+)", text).group(1)) == 1
+    assert L.asm_status_str(0) == b"ok"
+    assert L.asm_status_str(-5).startswith(b"workspace")
+
+
+NULL = None
+
+
+def _decode(**over):
+    args = dict(dtype=0, B=1, Hq=4, Hkv=2, d=128, K=16, scale=0.1, q=1 << 20, C=1 << 20,
+                cinv=1 << 20, Abar=1 << 20, LSEbar=1 << 20, Kl=1 << 20, Vl=1 << 20, hs=128 * 64,
+                ts=128, cap=64, ks=1 << 20, kn=1 << 20, m=64, out=1 << 20, lse=NULL, idx=NULL,
+                ws=NULL, wsb=0)
+    args.update(over)
+    a = args
+    L = api.lib()
+    return L.asm_decode_step(a["dtype"], a["B"], a["Hq"], a["Hkv"], a["d"], a["K"], a["scale"],
+                             a["q"], a["C"], a["cinv"], a["Abar"], a["LSEbar"], a["Kl"], a["Vl"],
+                             a["hs"], a["ts"], a["cap"], a["ks"], a["kn"], a["m"], a["out"],
+                             a["lse"], a["idx"], a["ws"], a["wsb"], None)
+
+
+def test_decode_validation_errors_before_any_launch():
+    L = api.lib()
+    assert _decode(dtype=5) == -3
+    assert _decode(Hq=6, Hkv=4) == -2
+    assert _decode(d=300) == -2
+    assert _decode(d=12) == -2          # bf16 rows must be multiples of 8
+    assert _decode(K=0) == -2
+    assert _decode(m=-1) == -2
+    assert _decode(q=NULL) == -1
+    assert _decode(Kl=NULL) == -1
+    assert _decode(ts=12) == -4         # bf16 stride not a multiple of 8
+    assert _decode(q=(1 << 20) + 2) == -4
+    assert _decode(scale=float("nan")) == -2
+    assert _decode() == -5              # a workspace is needed
+    assert b"workspace" in L.asm_last_error()
+    need = L.asm_decode_step_ws(0, 1, 4, 2, 128, 16, 64)
+    assert need > 0
+    assert _decode(ws=1 << 20, wsb=need - 1) == -5
+
+
+def test_workspace_sizes_follow_the_plan():
+    L = api.lib()
+    # keys (Hq * tiles * B * 8) + partial states (B * Hq * S * d * 4) + lse
+    assert L.asm_decode_step_ws(0, 32, 32, 8, 128, 8192, 4096) >= 32 * 32 * 32 * 8
+    assert L.asm_decode_step_ws(9, 32, 32, 8, 128, 8192, 4096) == 0  # invalid -> 0
+    assert L.asm_aggregate_ws(0, 32, 65536, 8192, 128) >= 4 * 32 * (65536 + 2 * 8192)
+
+
+def test_build_assign_aggregate_validation():
+    L = api.lib()
+    st = L.asm_build_states(0, 4, 3, 8, 16, 128, 4, 0.1, 1 << 20, 1 << 20, 1 << 20, None, None,
+                            1 << 20, 1 << 20, 0, None, 0, None)
+    assert st == -2  # Hq % Hkv
+    st = L.asm_build_states(0, 4, 2, 8, 16, 128, 4, 0.1, 1 << 20, 1 << 20, 1 << 20, 1 << 20, None,
+                            1 << 20, 1 << 20, 0, None, 0, None)
+    assert st == -1  # A_chunks without LSE_chunks
+    st = L.asm_build_states(0, 4, 2, 8, 16, 128, 0, 0.1, 1 << 20, 1 << 20, 1 << 20, None, None,
+                            1 << 20, 1 << 20, 0, None, 0, None)
+    assert st == -2  # chunk 0
+    assert L.asm_kmeans_assign(0, 2, 8, 0, 128, 1 << 20, 1 << 20, 1 << 20, 1 << 20, None, None, 0,
+                               None) == -2
+    assert L.asm_kmeans_assign(1, 2, 8, 4, 64, None, 1 << 20, 1 << 20, 1 << 20, None, None, 0,
+                               None) == -1
+    assert L.asm_aggregate(0, 2, 8, 4, 128, 1 << 20, 1 << 20, None, None, 1 << 20, 1 << 20,
+                           1 << 20, 1 << 20, None, None, 0, None) == -1  # Abar without LSEbar
+    assert L.asm_aggregate(0, 2, 8, 4, 128, 1 << 20, 1 << 20, None, None, 1 << 20, 1 << 20,
+                           1 << 20, None, None, None, 0, None) == -5  # no workspace
+    assert L.asm_centroid_inv_norms(3, 1, 1, 8, 1 << 20, 1 << 20, None) == -3
+    # empty problems are no-ops that succeed without touching the GPU
+    assert L.asm_centroid_inv_norms(0, 0, 5, 8, None, None, None) == 0
+    assert L.asm_kmeans_assign(0, 2, 0, 4, 128, None, None, None, None, None, None, 0, None) == 0
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    with pytest.raises(TypeError):
+        api.centroid_inv_norms(torch.zeros(1, 2, 8))
