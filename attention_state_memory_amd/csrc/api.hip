@@ -76,17 +76,33 @@ int check_ws(const void* ws, size_t ws_bytes, size_t need) {
 
 // ---- decode planning -------------------------------------------------------
 struct DecodePlan {
-  int split_tok = 0, S_max = 0, score_tiles = 0;
-  size_t off_keys = 0, off_pa = 0, off_pl = 0, total = 0;
+  bool fast = false;
+  int Bc = 0;  // sequences per launch
+  int n_waves = 0, uph = 0;                     // MFMA path
+  int split_tok = 0, S_max = 0, score_tiles = 0;  // VALU path
+  size_t off_keys = 0, off_tp = 0, off_pa = 0, off_pl = 0, total = 0;
 };
 
-int decode_split_tokens(int B, int Hkv, int max_kv_len) {
-  if (const char* e = getenv("ASM_DECODE_SPLIT")) {
+int env_int(const char* name, int fallback) {
+  if (const char* e = getenv(name)) {
     const int v = atoi(e);
-    if (v >= 32 && v % 32 == 0) return v;
+    if (v > 0) return v;
   }
-  // Aim for about 2048 attention items per step: enough to cover 256 CUs
-  // several times over while keeping the partial-state traffic small.
+  return fallback;
+}
+
+int device_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+    return 256;
+  return n;
+}
+
+int decode_split_tokens(int B, int Hkv, int max_kv_len) {
+  const int v = env_int("ASM_DECODE_SPLIT", 0);
+  if (v >= 32 && v % 32 == 0) return v;
+  // about 2048 attention items per step
   const int64_t work = int64_t(B) * Hkv * max_kv_len;
   int64_t s = (work + 2047) / 2048;
   s = (s + 127) / 128 * 128;
@@ -95,18 +111,45 @@ int decode_split_tokens(int B, int Hkv, int max_kv_len) {
   return int(s);
 }
 
-DecodePlan plan_decode(int B, int Hq, int Hkv, int d, int K, int max_kv_len) {
+DecodePlan plan_decode(int dtype, int B, int Hq, int Hkv, int d, int K, int max_kv_len,
+                       int64_t kv_tok_stride) {
   DecodePlan p;
-  p.split_tok = decode_split_tokens(B, Hkv, max_kv_len);
-  p.S_max = max_kv_len > 0 ? (max_kv_len + p.split_tok - 1) / p.split_tok : 0;
-  p.score_tiles = (K + 255) / 256;
+  const int G = Hq / Hkv;
+  p.fast = asmk::decode_fast_path(dtype, d, G, kv_tok_stride, max_kv_len);
   size_t off = 0;
-  p.off_keys = off;
-  off = asmk::align_up(off + size_t(Hq) * p.score_tiles * B * sizeof(uint64_t), kAlign);
-  p.off_pa = off;
-  off = asmk::align_up(off + size_t(B) * Hq * p.S_max * d * sizeof(float), kAlign);
-  p.off_pl = off;
-  off = asmk::align_up(off + size_t(B) * Hq * p.S_max * sizeof(float), kAlign);
+  if (p.fast) {
+    p.Bc = B < asmk::kFastMaxBatch ? B : asmk::kFastMaxBatch;
+    p.uph = (K + 63) / 64;
+    // Persistent grid: as many waves as fit on the device at once, but no
+    // more than about one per four work units (16 KB each).
+    const int64_t units = int64_t(Hq) * p.uph + int64_t(p.Bc) * Hkv * ((int64_t(max_kv_len) + 31) / 32);
+    const int64_t cap = int64_t(device_cus()) * asmk::decode_fast_waves_per_cu(d, G);
+    int64_t w = (units + 3) / 4;
+    w = env_int("ASM_DECODE_WAVES", int(w < cap ? w : cap));
+    w = (w + 3) / 4 * 4;
+    if (w < 4) w = 4;
+    p.n_waves = int(w);
+    p.off_keys = off;
+    off = asmk::align_up(off + size_t(Hq) * p.Bc * p.uph * sizeof(uint64_t), kAlign);
+    p.off_tp = off;
+    off = asmk::align_up(off + size_t(p.Bc + 1) * sizeof(int32_t), kAlign);
+    const size_t pieces = size_t(p.n_waves) + size_t(p.Bc) * Hkv;
+    p.off_pa = off;
+    off = asmk::align_up(off + pieces * G * d * sizeof(float), kAlign);
+    p.off_pl = off;
+    off = asmk::align_up(off + pieces * G * sizeof(float), kAlign);
+  } else {
+    p.Bc = B;
+    p.split_tok = decode_split_tokens(B, Hkv, max_kv_len);
+    p.S_max = max_kv_len > 0 ? (max_kv_len + p.split_tok - 1) / p.split_tok : 0;
+    p.score_tiles = (K + 255) / 256;
+    p.off_keys = off;
+    off = asmk::align_up(off + size_t(Hq) * p.score_tiles * B * sizeof(uint64_t), kAlign);
+    p.off_pa = off;
+    off = asmk::align_up(off + size_t(B) * Hq * p.S_max * d * sizeof(float), kAlign);
+    p.off_pl = off;
+    off = asmk::align_up(off + size_t(B) * Hq * p.S_max * sizeof(float), kAlign);
+  }
   p.total = off;
   return p;
 }
@@ -161,7 +204,11 @@ int asm_centroid_inv_norms(int dtype, int H, int K, int d, const void* C, float*
 // ---------------------------------------------------------------------------
 size_t asm_decode_step_ws(int dtype, int B, int Hq, int Hkv, int d, int K, int max_kv_len) {
   if (validate_decode_shape(dtype, B, Hq, Hkv, d, K, max_kv_len) != ASM_OK) return 0;
-  return plan_decode(B, Hq, Hkv, d, K, max_kv_len).total;
+  // The KV stride decides between the two layouts only at call time: size
+  // the workspace for whichever is larger.
+  const size_t fast = plan_decode(dtype, B, Hq, Hkv, d, K, max_kv_len, d).total;
+  const size_t slow = plan_decode(dtype, B, Hq, Hkv, d, K, max_kv_len, int64_t(1) << 40).total;
+  return fast > slow ? fast : slow;
 }
 
 int asm_decode_step(int dtype, int B, int Hq, int Hkv, int d, int K, float scale,
@@ -184,23 +231,39 @@ int asm_decode_step(int dtype, int B, int Hq, int Hkv, int d, int K, float scale
       return fail(ASM_ERR_ALIGN, "bf16 kv strides must be multiples of 8 elements");
   }
   ASM_TRY(check_bf16_ptrs(dtype, {q, C, Kl, Vl}));
-  const DecodePlan p = plan_decode(B, Hq, Hkv, d, K, max_kv_len);
+  const DecodePlan p = plan_decode(dtype, B, Hq, Hkv, d, K, max_kv_len, kv_tok_stride);
   ASM_TRY(check_ws(ws, ws_bytes, p.total));
 
   asmk::DecodeArgs a{};
-  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.d = d; a.K = K;
+  a.Hq = Hq; a.Hkv = Hkv; a.d = d; a.K = K;
   a.scale2 = scale * ASM_LOG2E;
-  a.q = q; a.C = C; a.cinv = cinv; a.Abar = Abar; a.LSEbar = LSEbar;
+  a.C = C; a.cinv = cinv; a.Abar = Abar; a.LSEbar = LSEbar;
   a.Kl = Kl; a.Vl = Vl;
   a.kv_head_stride = kv_head_stride; a.kv_tok_stride = kv_tok_stride; a.kv_capacity = kv_capacity;
-  a.kv_start = kv_start; a.kv_len = kv_len; a.max_kv_len = max_kv_len;
+  a.max_kv_len = max_kv_len;
+  a.n_waves = p.n_waves; a.uph = p.uph;
   a.split_tok = p.split_tok; a.S_max = p.S_max; a.score_tiles = p.score_tiles;
-  a.out = out; a.out_lse = out_lse; a.out_idx = out_idx;
   char* w = static_cast<char*>(ws);
   a.keys = reinterpret_cast<uint64_t*>(w + p.off_keys);
+  a.tile_prefix = reinterpret_cast<int32_t*>(w + p.off_tp);
   a.part_a = reinterpret_cast<float*>(w + p.off_pa);
   a.part_lse = reinterpret_cast<float*>(w + p.off_pl);
-  return hip_status(asmk::launch_decode(a, dtype, stream), "decode_step");
+  const size_t esz = dtype == ASM_BF16 ? 2 : 4;
+  // Sequences are independent: batches larger than one launch's limit run
+  // as consecutive launches over batch slices sharing the workspace.
+  for (int b0 = 0; b0 < B; b0 += p.Bc) {
+    const int nb = B - b0 < p.Bc ? B - b0 : p.Bc;
+    a.B = nb;
+    a.q = static_cast<const char*>(q) + size_t(b0) * Hq * d * esz;
+    a.kv_start = kv_start + b0;
+    a.kv_len = kv_len + b0;
+    a.out = out + size_t(b0) * Hq * d;
+    a.out_lse = out_lse ? out_lse + size_t(b0) * Hq : nullptr;
+    a.out_idx = out_idx ? out_idx + size_t(b0) * Hq : nullptr;
+    const int st = hip_status(asmk::launch_decode(a, dtype, stream), "decode_step");
+    if (st != ASM_OK) return st;
+  }
+  return ASM_OK;
 }
 
 // ---------------------------------------------------------------------------

@@ -43,6 +43,21 @@ __device__ __forceinline__ u32x4 ld16(const uint16_t* p) {
 }
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// Raw buffer resources: loads address base + voffset + soffset, and any
+// 16-byte load at or past num_records bytes returns zeros instead of touching
+// memory.  Ragged tails therefore need neither clamping nor branches, and the
+// per-lane offsets stay 32-bit and loop-invariant.
+constexpr int kBufferFlags = 0x00020000;  // raw buffer, 32-bit data format
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t num_bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, int(num_bytes), kBufferFlags);
+}
+__device__ __forceinline__ u32x4 buf16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+}
+__device__ __forceinline__ float buf_f32(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+}
+
 // Round a float64 to bf16, nearest with ties to even, in one step (no
 // intermediate float32 rounding).  bf16 keeps 8 significant bits and the
 // float32 exponent range; values whose rounded magnitude reaches 2^128
@@ -107,6 +122,33 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 __device__ __forceinline__ float readlane_f(float v, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+// Reductions across the 16 lanes of a DPP row (lanes 16r .. 16r+15) with DPP
+// moves instead of LDS permutes: quad swaps, then rotations by 4 and 8.  Every
+// lane of the row ends with the row's maximum; for the sum only the value
+// read back from one lane is used.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, false));
+}
+constexpr int kDppQuadXor1 = 0xB1;  // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;  // quad_perm [2,3,0,1]
+constexpr int kDppRowRor4 = 0x124;
+constexpr int kDppRowRor8 = 0x128;
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_mov<kDppQuadXor1>(v));
+  v = fmaxf(v, dpp_mov<kDppQuadXor2>(v));
+  v = fmaxf(v, dpp_mov<kDppRowRor4>(v));
+  v = fmaxf(v, dpp_mov<kDppRowRor8>(v));
+  return v;
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_mov<kDppQuadXor1>(v);
+  v += dpp_mov<kDppQuadXor2>(v);
+  v += dpp_mov<kDppRowRor4>(v);
+  v += dpp_mov<kDppRowRor8>(v);
+  return v;
 }
 
 // Orders LDS traffic between lanes of one wave without a workgroup barrier.

@@ -10,6 +10,10 @@
 namespace asmk {
 
 // ---- decode step ----------------------------------------------------------
+// Two workspace layouts exist.  The MFMA path (bf16, d in {64, 128},
+// Hq/Hkv in {1, 2, 4, 8}) balances the step over a persistent grid of
+// n_waves waves; the plain VALU path splits each sequence into fixed token
+// splits.
 struct DecodeArgs {
   int B, Hq, Hkv, d, K;
   float scale2;  // softmax scale * log2(e): scores are kept as base-2 logits
@@ -24,18 +28,27 @@ struct DecodeArgs {
   const int32_t* kv_start;
   const int32_t* kv_len;
   int max_kv_len;
-  int split_tok;    // local tokens per attention item
-  int S_max;        // splits per sequence = ceil(max_kv_len / split_tok)
-  int score_tiles;  // ceil(K / 256)
   float* out;
   float* out_lse;
   int32_t* out_idx;
-  uint64_t* keys;   // [Hq, score_tiles, B]
-  float* part_a;    // [B, Hq, S_max, d]
-  float* part_lse;  // [B, Hq, S_max]
+  // MFMA path
+  int n_waves;           // persistent waves (multiple of 4)
+  int uph;               // scoring units per head = ceil(K / 64)
+  int32_t* tile_prefix;  // [B + 1] 32-token tiles per kv head, prefix over sequences
+  // VALU path
+  int split_tok;    // local tokens per attention item
+  int S_max;        // splits per sequence = ceil(max_kv_len / split_tok)
+  int score_tiles;  // ceil(K / 256)
+  // both
+  uint64_t* keys;   // MFMA: [Hq, B, uph]; VALU: [Hq, score_tiles, B]
+  float* part_a;    // MFMA: [n_waves + B*Hkv, G, d]; VALU: [B, Hq, S_max, d]
+  float* part_lse;  // MFMA: [n_waves + B*Hkv, G];    VALU: [B, Hq, S_max]
 };
 
-bool decode_fast_path(int dtype, int d, int G);
+constexpr int kFastMaxBatch = 2048;  // sequences per MFMA-path launch
+bool decode_fast_path(int dtype, int d, int G, int64_t kv_tok_stride, int max_kv_len);
+int decode_fast_waves_per_cu(int d, int G);  // resident waves per CU of the MFMA main kernel
+hipError_t launch_decode_fast(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t s);
 
 // ---- centroid inverse norms -------------------------------------------------
