@@ -102,11 +102,13 @@ def _stream(device) -> ctypes.c_void_p:
 
 
 def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]) -> Optional[torch.Tensor]:
+    """The caller's workspace if large enough, else a new zero-filled one
+    (the decode workspace must start zeroed; calls leave it that way)."""
     if nbytes == 0:
         return ws
     if ws is not None and ws.numel() * ws.element_size() >= nbytes and ws.is_cuda:
         return ws
-    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return torch.zeros(nbytes, dtype=torch.uint8, device=device)
 
 
 def abi_version() -> int:

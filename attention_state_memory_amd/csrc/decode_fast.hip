@@ -310,8 +310,8 @@ __device__ __forceinline__ void attn_piece(const DecodeArgs& a, int b, int g, in
   using T = Tile<D, G>;
   const int lane = threadIdx.x & 63;
   const int r16 = lane & 15, grp = lane >> 4;
-  const int n = a.kv_len[b];
-  const int64_t st0 = a.kv_start[b];
+  const int n = __builtin_amdgcn_readfirstlane(a.kv_len[b]);
+  const int64_t st0 = __builtin_amdgcn_readfirstlane(a.kv_start[b]);
   const int64_t ts = a.kv_tok_stride;
   const uint32_t seg_bytes = uint32_t(n) * uint32_t(ts) * 2u;
   const auto rk = make_rsrc(static_cast<const uint16_t*>(a.Kl) + g * a.kv_head_stride + st0 * ts, seg_bytes);
@@ -428,7 +428,7 @@ decode_fast_main(DecodeArgs a) {
   const int64_t gw = int64_t(blockIdx.x) * 4 + w;
   const int64_t W = a.n_waves;
   const int64_t SU = int64_t(a.Hq) * a.uph;
-  const int64_t U = int64_t(tp[a.B]) * a.Hkv;
+  const int64_t U = int64_t(__builtin_amdgcn_readfirstlane(tp[a.B])) * a.Hkv;
 
   // scoring share first: every wave scores at the same time, so the table
   // streams with the whole grid's memory parallelism
@@ -442,14 +442,18 @@ decode_fast_main(DecodeArgs a) {
   int64_t t = gw < Wa ? share_lo(gw, U, Wa) : 0;
   const int64_t t_end = gw < Wa ? share_lo(gw + 1, U, Wa) : 0;
   while (t < t_end) {
+    // LDS reads land in vector registers; readfirstlane marks the (wave-
+    // uniform) values as scalars so the buffer resources built from them stay
+    // in SGPRs (otherwise every buffer load becomes a waterfall loop).
     int blo = 0, bhi = a.B;  // tp[blo]*Hkv <= t < tp[bhi]*Hkv
     while (bhi - blo > 1) {
       const int mid = (blo + bhi) >> 1;
-      if (int64_t(tp[mid]) * a.Hkv <= t) blo = mid; else bhi = mid;
+      if (int64_t(__builtin_amdgcn_readfirstlane(tp[mid])) * a.Hkv <= t) blo = mid; else bhi = mid;
     }
     const int b = blo;
-    const int nt = tp[b + 1] - tp[b];
-    const int64_t off = t - int64_t(tp[b]) * a.Hkv;
+    const int tb0 = __builtin_amdgcn_readfirstlane(tp[b]);
+    const int nt = __builtin_amdgcn_readfirstlane(tp[b + 1]) - tb0;
+    const int64_t off = t - int64_t(tb0) * a.Hkv;
     const int g = int(off / nt), j0 = int(off % nt);
     const int cnt = int(min<int64_t>(nt - j0, t_end - t));
     attn_piece<D, G, kPrefetch>(a, b, g, j0, j0 + cnt, gw + int64_t(b) * a.Hkv + g, pl);

@@ -89,7 +89,7 @@ def main():
     max_kv = 4096
     code = api.BF16
     ws_bytes = api.decode_step_ws(code, B, Hq, Hkv, d, K, max_kv)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
     out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
     out_lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
     out_idx = torch.empty((B, Hq), dtype=torch.int32, device=dev)
