@@ -54,6 +54,10 @@ def parse():
     p.add_argument("--no-graph", action="store_true", help="launch eagerly instead of a HIP graph")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="wall-clock budget of the CPU oracle baseline (0 disables it)")
+    p.add_argument("--workload", default="batched_decode",
+                   choices=("batched_decode", "prefix_states", "memory_build"),
+                   help="batched_decode (the headline metric) or one of the offline build "
+                        "workloads, reported on their MFMA rooflines")
     return p.parse_args()
 
 
@@ -63,6 +67,9 @@ def main():
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; "
                                    "multi-GPU runs are not part of this build"}))
         sys.exit(2)
+    if args.workload != "batched_decode":
+        run_build(args)
+        return
     import torch
     from attention_state_memory_amd import api, synth
 
@@ -206,6 +213,209 @@ def cpu_baseline(inp, budget_s: float) -> dict:
             "kind": "oracle",
             "sample": f"{passes} full decode step(s) of replica 0 ({B} sequences x "
                       f"{inp['Hq']} heads, K={inp['K']} scoring + local attention), {el:.1f} s"}
+
+
+# --------------------------------------------------------------------------
+# offline build workloads (MFMA-bound prefix states and k-means assignment)
+# --------------------------------------------------------------------------
+
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # dense bf16 / fp16 matrix peak of one MI355X
+
+
+def _timed(fn, reps):
+    """Mean milliseconds of fn() over reps calls, HIP events on the current stream."""
+    import torch
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def run_build(args):
+    import torch
+    from attention_state_memory_amd import api, synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def to_dev(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    if args.workload == "prefix_states":
+        w = synth.prefix_states()
+        Q, Kp, Vp = to_dev(w["Q"]), to_dev(w["Kp"]), to_dev(w["Vp"])
+        Hq, N, L, d, chunk = w["Hq"], w["N"], w["L"], w["d"], w["chunk"]
+        nc = -(-L // chunk)
+        A = torch.empty((Hq, N, d), dtype=torch.float32, device=dev)
+        LSE = torch.empty((Hq, N), dtype=torch.float32, device=dev)
+        Ac = torch.empty((nc, Hq, N, d), dtype=torch.float32, device=dev)
+        Lc = torch.empty((nc, Hq, N), dtype=torch.float32, device=dev)
+
+        L_ = api.lib()
+        ws_bytes = int(L_.asm_build_states_ws(api.BF16, Hq, w["Hkv"], N, L, d, chunk))
+        ws = torch.zeros(max(1, ws_bytes), dtype=torch.uint8, device=dev)
+        P = ctypes.c_void_p
+
+        def step_chunks():
+            # per-chunk states kept: the workload emits (a, lse) per chunk
+            st = L_.asm_build_states(api.BF16, Hq, w["Hkv"], N, L, d, chunk,
+                                     ctypes.c_float(w["scale"]),
+                                     *(P(t.data_ptr()) for t in (Q, Kp, Vp, Ac, Lc, A, LSE)),
+                                     0, P(ws.data_ptr()), ws_bytes,
+                                     P(torch.cuda.current_stream().cuda_stream))
+            if st != 0:
+                raise RuntimeError(L_.asm_last_error().decode())
+
+        for _ in range(args.warmup):
+            step_chunks()
+        steps = args.steps
+        ms = _timed(step_chunks, steps)
+        flops = 4.0 * Hq * N * L * d
+        tflops = flops / (ms * 1e-3) / 1e12
+        result = {
+            "metric": "prefix attention states (query-heads x prefix tokens) per second",
+            "value": Hq * N / (ms * 1e-3), "unit": "query-head states/s", "n_gpus": 1,
+            "steps": steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic (seeded 64-centre mixture queries, N(0,1) bf16 prefix)",
+            "config": {"workload": "prefix_states", "q_heads": Hq, "kv_heads": w["Hkv"],
+                       "head_dim": d, "queries_per_head": N, "prefix": L, "chunk": chunk,
+                       "per_chunk_states": True},
+            "roofline": {"bound": "mfma", "achieved": tflops, "peak": BF16_MFMA_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": tflops / BF16_MFMA_PEAK_TFLOPS,
+                         "traffic": None, "algorithmic_flops_per_launch": flops,
+                         "timed": "asm_build_states (one kernel launch)"},
+        }
+        if args.cpu_seconds > 0:
+            result["cpu_baseline"] = cpu_baseline_states(w, args.cpu_seconds)
+        print(json.dumps(result), flush=True)
+        return
+
+    # memory_build: states over the prefix, 10 Lloyd iterations, aggregation
+    w = synth.memory_build()
+    print("memory_build inputs generated", file=sys.stderr, flush=True)
+    H, N, K, d, T = w["Hq"], w["N"], w["K"], w["d"], w["iters"]
+    X, Kp, Vp = to_dev(w["X"]), to_dev(w["Kp"]), to_dev(w["Vp"])
+    A = torch.empty((H, N, d), dtype=torch.float32, device=dev)
+    LSE = torch.empty((H, N), dtype=torch.float32, device=dev)
+    C = torch.empty((H, K, d), dtype=torch.bfloat16, device=dev)
+    cinv = torch.empty((H, K), dtype=torch.float32, device=dev)
+    idx = torch.empty((H, N), dtype=torch.int32, device=dev)
+    count = torch.empty((H, K), dtype=torch.int32, device=dev)
+    Abar = torch.empty((H, K, d), dtype=torch.float32, device=dev)
+    LSEbar = torch.empty((H, K), dtype=torch.float32, device=dev)
+    ev = {k: [] for k in ("states", "assign", "mean", "aggregate")}
+
+    def mark():
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()
+        return e
+
+    def build(record):
+        e = [mark()]
+        api.build_states(X, Kp, Vp, w["chunk"], w["scale"], A=A, LSE=LSE)
+        e.append(mark())
+        C.copy_(X[:, :K, :])
+        api.centroid_inv_norms(C, cinv=cinv)
+        marks = []
+        for t in range(T):
+            a0 = mark()
+            api.kmeans_assign(X, C, cinv, idx=idx)
+            a1 = mark()
+            last = t == T - 1
+            api.aggregate(X, idx, C, A=A, LSE=LSE, cinv=cinv, count=count, Abar=Abar,
+                          LSEbar=LSEbar, with_states=last)
+            a2 = mark()
+            marks.append((a0, a1, a2, last))
+        e.append(mark())
+        if record:
+            torch.cuda.synchronize()
+            ev["states"].append(e[0].elapsed_time(e[1]))
+            for a0, a1, a2, last in marks:
+                ev["assign"].append(a0.elapsed_time(a1))
+                ev["aggregate" if last else "mean"].append(a1.elapsed_time(a2))
+            return e[0].elapsed_time(e[2])
+        return None
+
+    for _ in range(max(1, args.warmup)):
+        build(False)
+    torch.cuda.synchronize()
+    steps = max(1, args.steps)
+    totals = [build(True) for _ in range(steps)]
+    ms = float(np.mean(totals))
+    assign_ms = float(np.mean(ev["assign"]))
+    aflops = 2.0 * H * N * K * d
+    atf = aflops / (assign_ms * 1e-3) / 1e12
+    sflops = 4.0 * H * N * w["L"] * d
+    result = {
+        "metric": "ASM memory build wall-clock (states + 10 Lloyd iterations + aggregation)",
+        "value": ms * 1e-3, "unit": "s", "n_gpus": 1, "steps": steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded 64-centre mixture queries, N(0,1) bf16 prefix)",
+        "config": {"workload": "memory_build", "q_heads": H, "head_dim": d,
+                   "queries_per_head": N, "K": K, "iterations": T, "prefix": w["L"],
+                   "chunk": w["chunk"]},
+        "kernels_ms": {k: float(np.mean(v)) for k, v in ev.items()},
+        "states_tflops": sflops / (float(np.mean(ev["states"])) * 1e-3) / 1e12,
+        "roofline": {"bound": "mfma", "achieved": atf, "peak": BF16_MFMA_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": atf / BF16_MFMA_PEAK_TFLOPS, "traffic": None,
+                     "algorithmic_flops_per_launch": aflops,
+                     "timed": "asm_kmeans_assign (one kernel launch), mean of all iterations"},
+    }
+    if args.cpu_seconds > 0:
+        result["cpu_baseline"] = cpu_baseline_assign(w, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def _blas_threads():
+    from threadpoolctl import threadpool_info
+    return int(max((p.get("num_threads", 1) for p in threadpool_info()), default=1))
+
+
+def cpu_baseline_states(w, budget_s: float) -> dict:
+    from oracle import asm_oracle as O
+    Kp, Vp = O.bf16_bits_to_f64(w["Kp"]), O.bf16_bits_to_f64(w["Vp"])
+    rows = 64
+    t0 = time.perf_counter()
+    done = 0
+    while done == 0 or (time.perf_counter() - t0) < budget_s:
+        lo = (done * rows) % w["N"]
+        Q = O.bf16_bits_to_f64(w["Q"][:, lo:lo + rows])
+        O.build_states(Q, Kp, Vp, w["chunk"], w["scale"])
+        done += 1
+    el = time.perf_counter() - t0
+    return {"value": done * rows * w["Hq"] / el, "unit": "query-head states/s",
+            "cores": _blas_threads(), "kind": "oracle",
+            "sample": f"{done} pass(es) of {rows} queries x {w['Hq']} heads over the full "
+                      f"16384-token prefix in 4 chunks, {el:.1f} s"}
+
+
+def cpu_baseline_assign(w, budget_s: float) -> dict:
+    """The oracle's cosine assignment on row blocks of the first head against
+    the first-K centroids; reported as seconds per full assignment pass."""
+    from oracle import asm_oracle as O
+    X = w["X"]
+    K = w["K"]
+    C = O.bf16_bits_to_f64(X[0, :K])
+    rows = 256
+    t0 = time.perf_counter()
+    done = 0
+    while done == 0 or (time.perf_counter() - t0) < budget_s:
+        lo = (done * rows) % w["N"]
+        O.assign(O.bf16_bits_to_f64(X[0, lo:lo + rows]), C)
+        done += 1
+    el = time.perf_counter() - t0
+    per_row = el / (done * rows)
+    total = per_row * w["N"] * w["Hq"]
+    return {"value": total, "unit": "s per assignment pass (all heads, extrapolated)",
+            "cores": _blas_threads(), "kind": "oracle",
+            "sample": f"{done} block(s) of {rows} rows x K={K} of head 0, {el:.1f} s; "
+                      f"one full pass = {w['N']} rows x {w['Hq']} heads"}
 
 
 if __name__ == "__main__":

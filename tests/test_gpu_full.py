@@ -1,0 +1,108 @@
+"""GPU parity of the offline build at full size.
+
+* Prefix-state collection: 32 query heads x 4096 calibration queries over a
+  16384-token prefix cut into 4 chunks of 4096.  Every query's merged state is
+  checked against a monolithic single-chunk pass on the GPU (the chunk-split
+  identity of the online-softmax merge), and a seeded sample of 256 queries
+  per head is checked chunk by chunk against the fp64 oracle.
+* Memory build: 65536 collected queries per head, K = 8192, 10 Lloyd
+  iterations, then the Z-weighted aggregation of the final partition.  The
+  oracle is teacher-forced: at every iteration the GPU's assignment of a
+  seeded row sample is checked against the oracle's cosine argmax over the
+  GPU's previous centroids, every count against the member count of the GPU's
+  assignment, and the means of a seeded cluster sample bit for bit against the
+  oracle's mean step; the final states of the sampled clusters against the
+  oracle's aggregation of the GPU's final partition.  The input states come
+  from the GPU's prefix-state pass and are spot-checked on 256 queries per
+  head.
+"""
+import numpy as np
+import pytest
+import torch
+
+from attention_state_memory_amd import api, synth
+from oracle import asm_oracle as O
+from tests.helpers import A_TOL, LSE_TOL, assert_states_close, check_indices, dev, host, widen
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+
+def _sample(seed, n, k):
+    return np.sort(np.random.default_rng([300, *seed]).choice(n, size=k, replace=False))
+
+
+def _take(t, dim, rows):
+    return t.index_select(dim, torch.from_numpy(rows).to(t.device))
+
+
+def _check_prefix_sample(Q, Kp, Vp, A, LSE, chunk, scale, rows, Ac=None, Lc=None):
+    """Oracle states of Q[:, rows] against the GPU's, chunk by chunk when the
+    per-chunk states are given."""
+    Ac_ref, Lc_ref, A_ref, L_ref = O.build_states(widen(Q[:, rows]), widen(Kp), widen(Vp), chunk,
+                                                  scale)
+    assert_states_close(host(_take(A, 1, rows)), host(_take(LSE, 1, rows)), A_ref, L_ref)
+    if Ac is not None:
+        assert_states_close(host(_take(Ac, 2, rows)), host(_take(Lc, 2, rows)), Ac_ref, Lc_ref)
+
+
+@pytest.mark.timeout(900)
+def test_prefix_states_16k_prefix_4_chunks():
+    p = synth.prefix_states()
+    Q, Kp, Vp = dev(p["Q"]), dev(p["Kp"]), dev(p["Vp"])
+    A, LSE, Ac, Lc = api.build_states(Q, Kp, Vp, p["chunk"], p["scale"], keep_chunks=True)
+    A1, L1, _, _ = api.build_states(Q, Kp, Vp, p["L"], p["scale"])
+    torch.cuda.synchronize()
+    assert Ac.shape == (4, 32, 4096, 128)
+    # merged chunk states == one pass over the whole prefix, for every query
+    da = (A - A1).abs().max().item()
+    dl = (LSE - L1).abs().max().item()
+    assert torch.isfinite(A).all() and torch.isfinite(LSE).all()
+    assert da <= A_TOL and dl <= LSE_TOL, (da, dl)
+    rows = _sample([1], p["N"], 256)
+    _check_prefix_sample(p["Q"], p["Kp"], p["Vp"], A, LSE, p["chunk"], p["scale"], rows, Ac, Lc)
+    _check_prefix_sample(p["Q"], p["Kp"], p["Vp"], A1, L1, p["L"], p["scale"], rows)
+
+
+@pytest.mark.timeout(1200)
+def test_memory_build_65536_queries_K8192_10_iterations():
+    m = synth.memory_build()
+    H, N, K, d, T = m["Hq"], m["N"], m["K"], m["d"], m["iters"]
+    Xh = m["X"]
+    X = dev(Xh)
+    A, LSE, _, _ = api.build_states(X, dev(m["Kp"]), dev(m["Vp"]), m["chunk"], m["scale"])
+    torch.cuda.synchronize()
+    _check_prefix_sample(Xh, m["Kp"], m["Vp"], A, LSE, m["chunk"], m["scale"], _sample([2], N, 256))
+
+    C = X[:, :K, :].clone()
+    cinv = api.centroid_inv_norms(C)
+    count = torch.empty((H, K), dtype=torch.int32, device=X.device)
+    flips = 0
+    for t in range(T):
+        C_prev = host(C)
+        idx, _ = api.kmeans_assign(X, C, cinv)
+        last = t == T - 1
+        _, _, _, Abar, LSEbar = api.aggregate(X, idx, C, A=A, LSE=LSE, cinv=cinv, count=count,
+                                              with_states=last)
+        torch.cuda.synchronize()
+        idx_h, C_h, n_h, cinv_h = host(idx), host(C), host(count), host(cinv)
+        rows = _sample([3, t], N, 512)
+        for h in range(H):
+            # assignment of sampled rows against the oracle over the GPU's C^{t-1}
+            flips += check_indices(idx_h[h, rows], widen(Xh[h, rows]), widen(C_prev[h]))
+            # counts: the number of rows the GPU assigned to each cluster
+            np.testing.assert_array_equal(n_h[h], np.bincount(idx_h[h], minlength=K))
+            # means of sampled clusters (plus the largest), bit for bit
+            ks = np.union1d(_sample([4, t, h], K, 64), [int(np.argmax(n_h[h]))])
+            sel = np.isin(idx_h[h], ks)
+            remap = np.searchsorted(ks, idx_h[h, sel])
+            C_ref, n_ref = O.centroid_update(widen(Xh[h, sel]), remap, widen(C_prev[h, ks]), "bf16")
+            np.testing.assert_array_equal(n_h[h, ks], n_ref)
+            np.testing.assert_array_equal(widen(C_h[h, ks]), C_ref)
+            np.testing.assert_allclose(cinv_h[h, ks], O.inv_norms(C_ref), rtol=1e-6)
+            if last:
+                Ab_ref, Lb_ref = O.aggregate(host(A[h])[sel].astype(np.float64),
+                                             host(LSE[h])[sel].astype(np.float64), remap, ks.size)
+                assert_states_close(host(Abar[h])[ks], host(LSEbar[h])[ks], Ab_ref, Lb_ref,
+                                    a_tol=1e-5, lse_tol=1e-5)
+    # near-tie flips are legitimate but must stay rare
+    assert flips <= T * H * 512 // 100, flips
