@@ -102,8 +102,7 @@ def _stream(device) -> ctypes.c_void_p:
 
 
 def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]) -> Optional[torch.Tensor]:
-    """The caller's workspace if large enough, else a new zero-filled one
-    (the decode workspace must start zeroed; calls leave it that way)."""
+    """The caller's workspace if large enough, else a new one."""
     if nbytes == 0:
         return ws
     if ws is not None and ws.numel() * ws.element_size() >= nbytes and ws.is_cuda:

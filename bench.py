@@ -28,6 +28,50 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+COPY_CALIBRATION_ELEMS = 64 << 20  # float32 elements: 256 MiB read and 256 MiB written
+
+
+def copy_calibration(torch, dev):
+    """A plain streaming copy of known size (elementwise negation, float32),
+    whose FETCH_SIZE / WRITE_SIZE readings calibrate the byte counters."""
+    src = torch.ones(COPY_CALIBRATION_ELEMS, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def measured_traffic(profile_name: str, sources) -> dict:
+    """HBM bytes per step from the committed counter summary, if it was taken
+    on the kernel sources as they are now (else None: the kernel changed)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", profile_name)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    h = hashlib.sha256()
+    for src in sources:
+        with open(os.path.join(ROOT, src), "rb") as f:
+            h.update(f.read())
+    if fields.get("source_sha256") != h.hexdigest():
+        return None
+    try:
+        return {"bytes_per_step": float(fields["traffic_bytes_per_step"]),
+                "profile": f"profiles/{profile_name}"}
+    except (KeyError, ValueError):
+        return None
+
+
+DECODE_SOURCES = ("attention_state_memory_amd/csrc/decode_fast.hip",
+                  "attention_state_memory_amd/csrc/common.hpp",
+                  "attention_state_memory_amd/csrc/kernels.hpp",
+                  "attention_state_memory_amd/csrc/api.hip")
 
 
 def algorithmic_bytes(inp) -> int:
@@ -54,6 +98,9 @@ def parse():
     p.add_argument("--no-graph", action="store_true", help="launch eagerly instead of a HIP graph")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="wall-clock budget of the CPU oracle baseline (0 disables it)")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="run one plain device copy (256 MiB read, 256 MiB written) before the "
+                        "timed region, as the reference kernel for HBM byte counters")
     p.add_argument("--workload", default="batched_decode",
                    choices=("batched_decode", "prefix_states", "memory_build"),
                    help="batched_decode (the headline metric) or one of the offline build "
@@ -75,6 +122,8 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        copy_calibration(torch, dev)
 
     def to_dev(x):
         x = np.ascontiguousarray(x)
@@ -158,6 +207,7 @@ def main():
     qps = queries / (ms_step * 1e-3)
     alg_bytes = float(np.mean([algorithmic_bytes(h) for h in host_inputs]))
     achieved = alg_bytes / (ms_step * 1e-3) / 1e9
+    traffic = measured_traffic("decode_batched_K8192_traffic.txt", DECODE_SOURCES)
 
     result = {
         "metric": "ASM decode queries/sec (heads x tokens) at K=8192; achieved HBM GB/s vs peak",
@@ -176,9 +226,12 @@ def main():
                    "kv_heads": Hkv, "head_dim": d, "local_len": "U{512..4096}",
                    "replicas": R, "launch": "eager" if graph is None else "hip_graph"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic["bytes_per_step"] if traffic else None,
                      "algorithmic_bytes_per_step": alg_bytes,
-                     "timed": "whole decode step (fused main kernel + combine kernel)"},
+                     "kernel": "asm_decode_step = decode_fast_main + decode_fast_combine",
+                     "timed": "HIP events around every decode step on its stream; each step is "
+                              "the two launches of one asm_decode_step call"},
     }
 
     # ---- CPU baseline: the fp64 oracle, bounded sample of the same workload

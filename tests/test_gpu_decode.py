@@ -124,6 +124,26 @@ def test_decode_strided_kv_and_determinism():
     check_decode(inp, host(r1[0]), host(r1[1]), host(r1[2]))
 
 
+def test_decode_shared_workspace_across_shapes():
+    """One workspace serves calls of different shapes in turn; each result is
+    bit-identical to the same call on a fresh zeroed workspace."""
+    cases = [
+        _case(21, 128, 32, 8, 1000, [0, 37, 300]),
+        _case(22, 128, 32, 8, 1024, [2048]),          # one sequence over many waves
+        _case(23, 64, 16, 8, 513, [1, 31, 32, 33, 129]),
+        _case(24, 128, 16, 2, 257, [700, 64]),
+    ]
+    nbytes = max(api.decode_step_ws(0, c["B"], c["Hq"], c["Hkv"], c["d"], c["K"], 4096)
+                 for c in cases)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    for c in cases + cases[:1]:
+        shared = run_decode_gpu(c, max_kv_len=4096, workspace=ws)
+        fresh = run_decode_gpu(c, max_kv_len=4096)
+        for x, y in zip(shared, fresh):
+            np.testing.assert_array_equal(x, y)
+        check_decode(c, *shared)
+
+
 def test_centroid_inv_norms_match_definition():
     rng = np.random.default_rng([100, 12])
     C = synth.to_bf16_bits(rng.standard_normal((3, 777, 128)).astype(np.float32))
