@@ -268,15 +268,17 @@ int asm_decode_step(int dtype, int B, int Hq, int Hkv, int d, int K, float scale
 
 // ---------------------------------------------------------------------------
 size_t asm_build_states_ws(int dtype, int Hq, int Hkv, int N, int L, int d, int chunk) {
-  (void)dtype; (void)Hq; (void)Hkv; (void)N; (void)L; (void)d; (void)chunk;
-  return 0;
+  (void)chunk;
+  if (check_dtype(dtype) != ASM_OK || check_d(dtype, d) != ASM_OK || Hq < 1 || Hkv < 1 ||
+      Hq % Hkv != 0 || N < 0 || L < 0)
+    return 0;
+  return asmk::states_ws_bytes(dtype, Hq, Hkv, N, L, d);
 }
 
 int asm_build_states(int dtype, int Hq, int Hkv, int N, int L, int d, int chunk, float scale,
                      const void* Q, const void* Kp, const void* Vp,
                      float* A_chunks, float* LSE_chunks, float* A, float* LSE, int accumulate,
                      void* ws, size_t ws_bytes, hipStream_t stream) {
-  (void)ws; (void)ws_bytes;
   ASM_TRY(check_dtype(dtype));
   ASM_TRY(check_d(dtype, d));
   if (Hq < 1 || Hkv < 1 || N < 0 || L < 0 || chunk < 1)
@@ -291,6 +293,8 @@ int asm_build_states(int dtype, int Hq, int Hkv, int N, int L, int d, int chunk,
   if (!Q || !A || !LSE) return fail(ASM_ERR_NULL, "Q, A and LSE are required");
   if (L > 0 && (!Kp || !Vp)) return fail(ASM_ERR_NULL, "Kp and Vp are required when L > 0");
   ASM_TRY(check_bf16_ptrs(dtype, {Q, Kp, Vp}));
+  const size_t need = asmk::states_ws_bytes(dtype, Hq, Hkv, N, L, d);
+  ASM_TRY(check_ws(ws, ws_bytes, need));
   asmk::StatesArgs a{};
   a.Hq = Hq; a.Hkv = Hkv; a.N = N; a.L = L; a.d = d; a.chunk = chunk;
   a.nc = L > 0 ? int((int64_t(L) + chunk - 1) / chunk) : 0;
@@ -298,6 +302,7 @@ int asm_build_states(int dtype, int Hq, int Hkv, int N, int L, int d, int chunk,
   a.Q = Q; a.Kp = Kp; a.Vp = Vp;
   a.A_chunks = A_chunks; a.LSE_chunks = LSE_chunks; a.A = A; a.LSE = LSE;
   a.accumulate = accumulate ? 1 : 0;
+  a.V16 = need > 0 ? ws : nullptr;
   return hip_status(asmk::launch_build_states(a, dtype, stream), "build_states");
 }
 

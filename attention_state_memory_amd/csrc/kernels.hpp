@@ -67,8 +67,10 @@ struct StatesArgs {
   float* A;
   float* LSE;
   int accumulate;
+  void* V16;  // MFMA path: Vp converted to fp16 [Hkv, L, d] (workspace)
 };
 bool states_fast_path(int dtype, int d, int G);
+size_t states_ws_bytes(int dtype, int Hq, int Hkv, int N, int L, int d);  // 0: VALU path
 hipError_t launch_build_states(const StatesArgs& a, int dtype, hipStream_t s);
 hipError_t launch_states_generic(const StatesArgs& a, int dtype, hipStream_t s);
 

@@ -7,19 +7,23 @@
 // (the prefix is cut into chunks whose states are merged with the
 // online-softmax identity).
 //
-// A workgroup holds four waves that share one kv head's K/V tiles: wave w
+// A workgroup holds eight waves (two per SIMD, so one wave's softmax overlaps
+// the other's matrix work) that share one kv head's K/V tiles: wave w
 // computes the states of 32 queries of one query head.  Per 64-key tile:
 //   S^T = K Q^T      (16x16x32 bf16 MFMA; A = K rows from LDS, B = the
 //                     wave's queries in registers), so every lane's scores
 //                     belong to one query column and the online softmax
 //                     needs no register transposes;
-//   O^T += V^T P^T   (16x16x32 f16 MFMA; A = V^T read from an LDS copy of the
-//                     tile transposed to [dim][key] in fp16, B = the
-//                     probabilities, already in the B-operand layout).
+//   O^T += V^T P^T   (16x16x32 f16 MFMA; A = V^T, gathered from the
+//                     row-major fp16 V tile in LDS by transposing reads
+//                     (ds_read_b64_tr_b16), B = the probabilities, already
+//                     in the B-operand layout).
 // The probability-value products run in fp16: P <= 1 and fp16 keeps 3 more
-// mantissa bits than bf16; V values must stay below 65504.  At each chunk
+// mantissa bits than bf16; V is converted to fp16 once per call into the
+// workspace, so its values must stay below 65504.  At each chunk
 // boundary the chunk state (O/l, m + log l) is written (if requested) and
-// merged into the running state in registers.
+// merged into the running state, which lives in the output (A, LSE) between
+// chunks: every wave reads back only rows it wrote itself.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -29,17 +33,19 @@ namespace {
 
 constexpr int kKeys = 64;        // keys per LDS tile
 constexpr int kQ = 32;           // queries per wave (two MFMA column tiles)
+constexpr int kWaves = 8;        // waves per workgroup
+constexpr int kThreads = 64 * kWaves;
 
 template <int D>
 struct StatesSmem {
   static constexpr int kKRow = D * 2 + 16;           // padded K row (bf16)
-  static constexpr int kVRow = kKeys * 2 + 8;        // padded V^T row (fp16)
+  static constexpr int kVRow = D * 2 + 32;           // padded V row (fp16)
   static constexpr int kKBytes = kKeys * kKRow;
-  static constexpr int kVBytes = D * kVRow;
+  static constexpr int kVBytes = kKeys * kVRow;
   static constexpr int kBuf = kKBytes + kVBytes;
   static constexpr int kBytes = 2 * kBuf;
-  static constexpr int kKChunks = kKeys * D / 8 / 256;  // 16-byte K pieces per thread
-  static constexpr int kVChunks = kKeys * D / 8 / 256;
+  static constexpr int kKChunks = kKeys * D / 8 / kThreads;  // 16-byte K pieces per thread
+  static constexpr int kVChunks = kKeys * D / 8 / kThreads;
 };
 
 template <int D>
@@ -55,48 +61,80 @@ __device__ __forceinline__ void stage_load(Staged<D>& r, __amdgpu_buffer_rsrc_t 
   constexpr int kPieces = D / 8;
 #pragma unroll
   for (int i = 0; i < StatesSmem<D>::kKChunks; ++i) {
-    const int c = threadIdx.x + 256 * i;
+    const int c = threadIdx.x + kThreads * i;
     const int key = c / kPieces, piece = c % kPieces;
     r.k[i] = buf16(rk, ((k0 + key) * D + piece * 8) * 2, 0);
   }
 #pragma unroll
   for (int i = 0; i < StatesSmem<D>::kVChunks; ++i) {
-    const int c = threadIdx.x + 256 * i;
-    const int key = c % kKeys, dd0 = 8 * (c / kKeys);
-    r.v[i] = buf16(rv, ((k0 + key) * D + dd0) * 2, 0);
+    const int c = threadIdx.x + kThreads * i;
+    const int key = c / kPieces, piece = c % kPieces;
+    r.v[i] = buf16(rv, ((k0 + key) * D + piece * 8) * 2, 0);
   }
 }
 
-// registers -> LDS: K row-major [key][d] (bf16); V transposed [d][key] (fp16)
+// registers -> LDS: K row-major [key][d] (bf16), V row-major [key][d] (fp16)
 template <int D>
 __device__ __forceinline__ void stage_store(char* buf, const Staged<D>& r) {
   using S = StatesSmem<D>;
   constexpr int kPieces = D / 8;
 #pragma unroll
   for (int i = 0; i < S::kKChunks; ++i) {
-    const int c = threadIdx.x + 256 * i;
+    const int c = threadIdx.x + kThreads * i;
     const int key = c / kPieces, piece = c % kPieces;
     *reinterpret_cast<u32x4*>(buf + key * S::kKRow + piece * 16) = r.k[i];
   }
-  _Float16* vt = reinterpret_cast<_Float16*>(buf + S::kKBytes);
 #pragma unroll
   for (int i = 0; i < S::kVChunks; ++i) {
-    const int c = threadIdx.x + 256 * i;
-    const int key = c % kKeys, dd0 = 8 * (c / kKeys);
+    const int c = threadIdx.x + kThreads * i;
+    const int key = c / kPieces, piece = c % kPieces;
+    *reinterpret_cast<u32x4*>(buf + S::kKBytes + key * S::kVRow + piece * 16) = r.v[i];
+  }
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// V^T operand of the value MFMA for dims 16*dt .. +15 and the 8 keys
+// {kb .. kb+3} and {kb2 .. kb2+3} (per lane group) of the tile in LDS.  A
+// transposing read over a 16-lane group returns, to lane j, element j % 16
+// of ... four consecutive rows: lane i of the group addresses row
+// kb + i / 4, dims 16*dt + 4*(i % 4) .. +3, and lane j receives dim
+// 16*dt + j of rows kb .. kb+3.
+template <int D>
+__device__ __forceinline__ f16x8 load_vt(const char* vbase, int dt, int kb, int kb2, int r16) {
+  using S = StatesSmem<D>;
+  const int roff = (r16 >> 2) * S::kVRow + (16 * dt + 4 * (r16 & 3)) * 2;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vbase + kb * S::kVRow + roff));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vbase + kb2 * S::kVRow + roff));
+  const u32x4 v = {__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
+                   __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]};
+  return __builtin_bit_cast(f16x8, v);
+}
+
+// bf16 -> fp16 (round to nearest even), eight values per thread
+__global__ void v_to_f16_kernel(const u32x4* src, u32x4* dst, int64_t n8) {
+  for (int64_t i = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; i < n8;
+       i += int64_t(gridDim.x) * blockDim.x) {
+    const u32x4 v = src[i];
+    u32x4 o;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      vt[(dd0 + 2 * e) * (S::kVRow / 2) + key] = (_Float16)bf16_lo(r.v[i][e]);
-      vt[(dd0 + 2 * e + 1) * (S::kVRow / 2) + key] = (_Float16)bf16_hi(r.v[i][e]);
+      const _Float16 lo = (_Float16)bf16_lo(v[e]);
+      const _Float16 hi = (_Float16)bf16_hi(v[e]);
+      o[e] = uint32_t(__builtin_bit_cast(uint16_t, lo)) | (uint32_t(__builtin_bit_cast(uint16_t, hi)) << 16);
     }
+    dst[i] = o;
   }
 }
 
 }  // namespace
 
 // GW query heads per workgroup share the K/V tiles (GW = min(G, 4)); the
-// workgroup covers 32 * 4 / GW queries of each of its heads.
+// workgroup covers 32 * 8 / GW queries of each of its heads.
 template <int D, int GW>
-__global__ void __launch_bounds__(256) states_mfma_kernel(StatesArgs a, int row_blocks, int hsubs) {
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+states_mfma_kernel(StatesArgs a, int row_blocks, int hsubs) {
   using S = StatesSmem<D>;
   constexpr int KS = D / 32;   // k-steps of the score MFMA
   constexpr int DT = D / 16;   // dim tiles of the value MFMA
@@ -109,10 +147,10 @@ __global__ void __launch_bounds__(256) states_mfma_kernel(StatesArgs a, int row_
   const int hs = (blockIdx.x / row_blocks) % hsubs;
   const int g = blockIdx.x / (row_blocks * hsubs);
   const int h = g * G + hs * GW + (w % GW);
-  const int q0 = rb * (kQ * 4 / GW) + kQ * (w / GW);  // first query of this wave
+  const int q0 = rb * (kQ * kWaves / GW) + kQ * (w / GW);  // first query of this wave
 
   const auto rk = make_rsrc(static_cast<const uint16_t*>(a.Kp) + size_t(g) * a.L * D, uint32_t(a.L) * D * 2);
-  const auto rv = make_rsrc(static_cast<const uint16_t*>(a.Vp) + size_t(g) * a.L * D, uint32_t(a.L) * D * 2);
+  const auto rv = make_rsrc(static_cast<const uint16_t*>(a.V16) + size_t(g) * a.L * D, uint32_t(a.L) * D * 2);
   const auto rq = make_rsrc(static_cast<const uint16_t*>(a.Q) + size_t(h) * a.N * D, uint32_t(a.N) * D * 2);
 
   // B operand of the score MFMA: query columns q0 + 16*qt + r16 (past N: zeros)
@@ -123,21 +161,7 @@ __global__ void __launch_bounds__(256) states_mfma_kernel(StatesArgs a, int row_
     for (int s = 0; s < KS; ++s)
       qb[qt][s] = as_bf16x8(buf16(rq, ((q0 + 16 * qt + r16) * D + 32 * s + 8 * grp) * 2, 0));
 
-  // running (merged) state, O^T layout: dim 16*dt + 4*grp + i, query 16*qt + r16
-  float R[DT][2][4];
-  float lseR[2];
   const bool acc_in = a.accumulate != 0;
-#pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
-    const int q = q0 + 16 * qt + r16;
-    const bool qv = q < a.N;
-    lseR[qt] = (acc_in && qv) ? a.LSE[size_t(h) * a.N + q] : -INFINITY;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        R[dt][qt][i] = (acc_in && qv) ? a.A[(size_t(h) * a.N + q) * D + 16 * dt + 4 * grp + i] : 0.0f;
-  }
 
   float O[DT][2][4];
   float m[2], l[2];
@@ -164,9 +188,12 @@ __global__ void __launch_bounds__(256) states_mfma_kernel(StatesArgs a, int row_
     for (int k0 = c_lo; k0 < c_hi; k0 += kKeys) {
       __syncthreads();  // tile k0 is in buffer buf_i; the other buffer is free
       char* cur = smem + buf_i * S::kBuf;
-      // the next tile: next keys of this chunk, else the first of the next chunk
-      const int nk = k0 + kKeys < c_hi ? k0 + kKeys : (c + 1 < nc ? c_hi : -1);
-      if (nk >= 0) stage_load<D>(stg, rk, rv, nk);
+      // the next tile: next keys of this chunk, else the first of the next
+      // chunk; after the last tile the loads start at L and read zeros.  The
+      // loads and the LDS store are never skipped, so the compiler's wait
+      // for them stays at the store.
+      const int nk = k0 + kKeys < c_hi ? k0 + kKeys : c_hi;
+      stage_load<D>(stg, rk, rv, nk);
       const int nvalid = min(kKeys, c_hi - k0);
 #pragma unroll
       for (int ks = 0; ks < kKeys / 32; ++ks) {
@@ -230,14 +257,10 @@ __global__ void __launch_bounds__(256) states_mfma_kernel(StatesArgs a, int row_
         }
         // O^T += V^T P^T over these 32 keys; the k index of lane group grp is
         // keys {4grp..4grp+3} then {16+4grp..16+4grp+3}, matching pb
-        const _Float16* vt = reinterpret_cast<const _Float16*>(cur + S::kKBytes);
+        const char* vbase = cur + S::kKBytes;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-          const _Float16* row = vt + (16 * dt + r16) * (S::kVRow / 2) + 32 * ks + 4 * grp;
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(row);
-          const u32x2 hi = *reinterpret_cast<const u32x2*>(row + 16);
-          const u32x4 vv = {lo[0], lo[1], hi[0], hi[1]};
-          const f16x8 va = __builtin_bit_cast(f16x8, vv);
+          const f16x8 va = load_vt<D>(vbase, dt, 32 * ks + 4 * grp, 32 * ks + 16 + 4 * grp, r16);
 #pragma unroll
           for (int qt = 0; qt < 2; ++qt) {
             f32x4 o = {O[dt][qt][0], O[dt][qt][1], O[dt][qt][2], O[dt][qt][3]};
@@ -247,7 +270,7 @@ __global__ void __launch_bounds__(256) states_mfma_kernel(StatesArgs a, int row_
           }
         }
       }
-      if (nk >= 0) stage_store<D>(smem + (buf_i ^ 1) * S::kBuf, stg);
+      stage_store<D>(smem + (buf_i ^ 1) * S::kBuf, stg);
       buf_i ^= 1;
     }
     // chunk state and running merge (per query column r16 of each qt)
@@ -271,34 +294,29 @@ __global__ void __launch_bounds__(256) states_mfma_kernel(StatesArgs a, int row_
         }
         if (grp == 0) a.LSE_chunks[row] = lse_c;
       }
-      const float M = fmaxf(lseR[qt], lse_c);
-      if (M != -INFINITY) {
-        const float w1 = lseR[qt] == -INFINITY ? 0.0f : expf(lseR[qt] - M);
+      // merge into the running state kept in (A, LSE); chunk 0 of a fresh
+      // build has no running state
+      if (q < a.N) {
+        const size_t row = size_t(h) * a.N + q;
+        const bool fresh = c == 0 && !acc_in;
+        const float lr = fresh ? -INFINITY : a.LSE[row];
+        const float M = fmaxf(lr, lse_c);
+        const float w1 = lr == -INFINITY ? 0.0f : expf(lr - M);
         const float w2 = empty ? 0.0f : expf(lse_c - M);
         const float z = w1 + w2;
-        const float iz = 1.0f / z;
+        const float iz = M == -INFINITY ? 0.0f : 1.0f / z;
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
+        for (int dt = 0; dt < DT; ++dt) {
+          float* ap = a.A + row * D + 16 * dt + 4 * grp;
+          const f32x4 r = fresh ? f32x4{0.f, 0.f, 0.f, 0.f} : *reinterpret_cast<const f32x4*>(ap);
+          f32x4 v;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) R[dt][qt][i] = (w1 * R[dt][qt][i] + w2 * O[dt][qt][i] * inv) * iz;
-        lseR[qt] = M + logf(z);
+          for (int i = 0; i < 4; ++i) v[i] = (w1 * r[i] + w2 * O[dt][qt][i] * inv) * iz;
+          *reinterpret_cast<f32x4*>(ap) = v;
+        }
+        if (grp == 0) a.LSE[row] = M == -INFINITY ? -INFINITY : M + logf(z);
       }
     }
-  }
-  // merged state
-#pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
-    const int q = q0 + 16 * qt + r16;
-    if (q >= a.N) continue;
-    const size_t row = size_t(h) * a.N + q;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      f32x4 v;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = lseR[qt] == -INFINITY ? 0.0f : R[dt][qt][i];
-      *reinterpret_cast<f32x4*>(a.A + row * D + 16 * dt + 4 * grp) = v;
-    }
-    if (grp == 0) a.LSE[row] = lseR[qt];
   }
 }
 
@@ -306,22 +324,31 @@ bool states_fast_path(int dtype, int d, int G) {
   return dtype == 0 && (d == 64 || d == 128) && (G == 1 || G == 2 || G == 4 || G == 8);
 }
 
+size_t states_ws_bytes(int dtype, int Hq, int Hkv, int N, int L, int d) {
+  if (!states_fast_path(dtype, d, Hq / Hkv) || L == 0 || N == 0) return 0;
+  if (int64_t(L + kKeys) * d * 2 >= (int64_t(1) << 31) || int64_t(N + kQ * kWaves) * d * 2 >= (int64_t(1) << 31))
+    return 0;
+  return (size_t(Hkv) * L * d * 2 + 255) / 256 * 256;
+}
+
 template <int D, int GW>
 static void launch_states(const StatesArgs& a, hipStream_t s) {
   const int G = a.Hq / a.Hkv;
-  const int rows = kQ * 4 / GW;
+  const int rows = kQ * kWaves / GW;
   const int row_blocks = (a.N + rows - 1) / rows;
   const int hsubs = G / GW;
   const dim3 grid(unsigned(row_blocks * hsubs * a.Hkv));
-  hipLaunchKernelGGL((states_mfma_kernel<D, GW>), grid, dim3(256), 0, s, a, row_blocks, hsubs);
+  hipLaunchKernelGGL((states_mfma_kernel<D, GW>), grid, dim3(kThreads), 0, s, a, row_blocks, hsubs);
 }
 
 hipError_t launch_build_states(const StatesArgs& a, int dtype, hipStream_t s) {
   const int G = a.Hq / a.Hkv;
-  const bool fits = int64_t(a.L + kKeys) * a.d * 2 < (int64_t(1) << 31) &&
-                    int64_t(a.N + kQ * 4) * a.d * 2 < (int64_t(1) << 31);
-  if (!states_fast_path(dtype, a.d, G) || !fits || a.L == 0 || a.N == 0)
+  if (states_ws_bytes(dtype, a.Hq, a.Hkv, a.N, a.L, a.d) == 0 || a.V16 == nullptr)
     return launch_states_generic(a, dtype, s);
+  const int64_t n8 = int64_t(a.Hkv) * a.L * a.d / 8;
+  const int64_t vb = (n8 + 255) / 256;
+  hipLaunchKernelGGL(v_to_f16_kernel, dim3(unsigned(vb < 8192 ? vb : 8192)), dim3(256), 0, s,
+                     static_cast<const u32x4*>(a.Vp), static_cast<u32x4*>(a.V16), n8);
   if (a.d == 128) {
     if (G == 1) launch_states<128, 1>(a, s);
     else if (G == 2) launch_states<128, 2>(a, s);
