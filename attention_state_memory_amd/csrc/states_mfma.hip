@@ -130,6 +130,48 @@ __global__ void v_to_f16_kernel(const u32x4* src, u32x4* dst, int64_t n8) {
 
 }  // namespace
 
+// Online softmax of one 32-key block for query column tile qt: scores
+// st[kk][qt][i] belong to key 32*ks + 16*kk + 4*grp + i.  The reference
+// maximum m is lazy: it only moves when the block's maximum exceeds it by
+// more than kLazy (base-2 units), so most blocks rescale nothing; the
+// probabilities then stay below 2^kLazy, far inside fp16.  Exponents are
+// exp2(s * scale2 - m) with one rounding (scale2 > 0).  Returns whether m
+// moved (then O must be scaled by alpha[qt]).
+constexpr float kLazy = 8.0f;
+
+template <bool kFull>
+__device__ __forceinline__ bool softmax_block(const f32x4 (&st)[2][2], int qt, int ks, int grp,
+                                              int nvalid, float scale2, float (&m)[2],
+                                              float (&l)[2], float (&alpha)[2], f16x8 (&pb)[2]) {
+  float mt = -INFINITY;
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool ok = kFull || 32 * ks + 16 * kk + 4 * grp + i < nvalid;
+      mt = fmaxf(mt, ok ? st[kk][qt][i] : -INFINITY);
+    }
+  mt = fmaxf(mt, shfl_xor_f(mt, 16));
+  mt = fmaxf(mt, shfl_xor_f(mt, 32));
+  const float mts = mt * scale2;
+  const bool up = mts > m[qt] + kLazy;  // always true for the first block
+  const float mn = up ? mts : m[qt];
+  alpha[qt] = up ? __builtin_amdgcn_exp2f(m[qt] - mn) : 1.0f;
+  float lp = 0.0f;
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool ok = kFull || 32 * ks + 16 * kk + 4 * grp + i < nvalid;
+      const float p = ok ? __builtin_amdgcn_exp2f(fmaf(st[kk][qt][i], scale2, -mn)) : 0.0f;
+      lp += p;
+      pb[qt][4 * kk + i] = (_Float16)p;
+    }
+  l[qt] = l[qt] * alpha[qt] + lp;
+  m[qt] = mn;
+  return up;
+}
+
 // GW query heads per workgroup share the K/V tiles (GW = min(G, 4)); the
 // workgroup covers 32 * 8 / GW queries of each of its heads.
 template <int D, int GW>
@@ -215,39 +257,14 @@ states_mfma_kernel(StatesArgs a, int row_blocks, int hsubs) {
           }
         }
         f16x8 pb[2];
-        bool rescale = false;
         float alpha[2];
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt) {
-          float sv[2][4];
-          float mt = -INFINITY;
-#pragma unroll
-          for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int key = 32 * ks + 16 * kk + 4 * grp + i;
-              sv[kk][i] = key < nvalid ? st[kk][qt][i] * a.scale2 : -INFINITY;
-              mt = fmaxf(mt, sv[kk][i]);
-            }
-          mt = fmaxf(mt, shfl_xor_f(mt, 16));
-          mt = fmaxf(mt, shfl_xor_f(mt, 32));
-          const float mn = fmaxf(m[qt], mt);
-          // a block of only masked keys (mn = -inf) leaves the state alone
-          alpha[qt] = mn == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m[qt] - mn);
-          rescale |= alpha[qt] != 1.0f;
-          float lp = 0.0f;
-#pragma unroll
-          for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const float p = mn == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(sv[kk][i] - mn);
-              lp += p;
-              pb[qt][4 * kk + i] = (_Float16)p;
-            }
-          l[qt] = l[qt] * alpha[qt] + lp;
-          m[qt] = mn;
-        }
-        if (__any(rescale)) {
+        const bool up0 = nvalid >= kKeys
+                             ? softmax_block<true>(st, 0, ks, grp, nvalid, a.scale2, m, l, alpha, pb)
+                             : softmax_block<false>(st, 0, ks, grp, nvalid, a.scale2, m, l, alpha, pb);
+        const bool up1 = nvalid >= kKeys
+                             ? softmax_block<true>(st, 1, ks, grp, nvalid, a.scale2, m, l, alpha, pb)
+                             : softmax_block<false>(st, 1, ks, grp, nvalid, a.scale2, m, l, alpha, pb);
+        if (__any(up0 || up1)) {
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -343,7 +360,7 @@ static void launch_states(const StatesArgs& a, hipStream_t s) {
 
 hipError_t launch_build_states(const StatesArgs& a, int dtype, hipStream_t s) {
   const int G = a.Hq / a.Hkv;
-  if (states_ws_bytes(dtype, a.Hq, a.Hkv, a.N, a.L, a.d) == 0 || a.V16 == nullptr)
+  if (states_ws_bytes(dtype, a.Hq, a.Hkv, a.N, a.L, a.d) == 0 || a.V16 == nullptr || !(a.scale2 > 0.0f))
     return launch_states_generic(a, dtype, s);
   const int64_t n8 = int64_t(a.Hkv) * a.L * a.d / 8;
   const int64_t vb = (n8 + 255) / 256;
