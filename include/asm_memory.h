@@ -135,8 +135,11 @@ int asm_decode_step(int dtype, int B, int Hq, int Hkv, int d, int K, float scale
  *     the incoming (A, LSE) are merged with this call's prefix states (a
  *     prefix streamed in pieces); otherwise they are overwritten.
  *   d in {64, 128} for bf16 (any 1..256 for float32).
- *   bf16 builds take the value products in fp16 (see the design notes):
- *   |Vp| must stay below 65504.
+ *   bf16 builds with d in {64, 128} and Hq/Hkv in {1, 2, 4, 8} convert Vp
+ *   to fp16 once per call into the workspace (asm_build_states_ws bytes,
+ *   Hkv*L*d*2 rounded up to 256) and take the probability-value products in
+ *   fp16 with float32 accumulation: |Vp| must stay below 65504.  Other
+ *   shapes need no workspace.
  */
 size_t asm_build_states_ws(int dtype, int Hq, int Hkv, int N, int L, int d, int chunk);
 int asm_build_states(int dtype, int Hq, int Hkv, int N, int L, int d, int chunk, float scale,
