@@ -144,6 +144,25 @@ def test_decode_shared_workspace_across_shapes():
         check_decode(c, *shared)
 
 
+def test_decode_batch_beyond_one_launch():
+    """2100 sequences: more than one launch's batch on the MFMA path, so the
+    call runs as consecutive launches over batch slices sharing the
+    workspace.  Short ragged contexts (0..64 tokens) keep the oracle cheap."""
+    rng = np.random.default_rng([100, 30])
+    lens = rng.integers(0, 65, 2100)
+    inp = synth.decode_inputs([100, 31], B=2100, Hq=8, Hkv=2, d=128, K=96, kv_lens=lens)
+    out, lse, idx = run_decode_gpu(inp, max_kv_len=64)
+    check_decode(inp, out, lse, idx)
+
+
+def test_decode_one_sequence_long_context_many_pieces():
+    """Batch 1 with a 40000-token context: the segment is split over many
+    waves (dozens of partial states merged by the combine)."""
+    inp = _case(32, 128, 32, 8, 512, [40000])
+    out, lse, idx = run_decode_gpu(inp)
+    check_decode(inp, out, lse, idx)
+
+
 def test_centroid_inv_norms_match_definition():
     rng = np.random.default_rng([100, 12])
     C = synth.to_bf16_bits(rng.standard_normal((3, 777, 128)).astype(np.float32))
