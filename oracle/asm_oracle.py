@@ -412,3 +412,63 @@ def decode(q, C, Abar, LSEbar, K_loc, V_loc, scale: float):
         idx[:, h], cs[:, h], gap[:, h] = i, c, g
     out, out_lse = decode_with_idx(q, idx, Abar, LSEbar, K_loc, V_loc, scale)
     return out, out_lse, idx, cs, gap
+
+
+# --------------------------------------------------------------------------
+# Hierarchical lookup
+# [TS] Complejidad: the lookup cost grows with the logarithm of the memory
+# size through a hierarchical index.  The pages say no more; the reading
+# taken is a two-level index.  The K entry queries of a head are clustered,
+# with the build's own cosine k-means (first-S initialisation, means rounded
+# to the table's type), into S super-centroids.  A query scores the S
+# supers, probes the p best non-empty ones (lowest index on ties) and takes
+# the entry of highest cosine among their members (lowest entry index on
+# ties).  Probing every non-empty super is the flat search.
+# --------------------------------------------------------------------------
+
+
+def build_index(C, S: int, iters: int, dtype: str):
+    """Super-centroids of the entry queries C [K, d] of one head.
+
+    Returns (SC [S, d], e2s [K] super of every entry, counts [S]): the
+    partition is the last assignment, whose means are SC."""
+    SC, e2s, counts = lloyd(np.asarray(C, np.float64), S, iters, dtype)
+    return SC, e2s, counts
+
+
+def index_members(e2s, S: int):
+    """(offsets [S+1], members [K]): the entries of super s are
+    members[offsets[s]:offsets[s+1]], in ascending order."""
+    e2s = np.asarray(e2s).astype(np.int64)
+    counts = np.bincount(e2s, minlength=S)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    members = np.argsort(e2s, kind="stable").astype(np.int64)
+    return offsets, members
+
+
+def probe_supers(q, SC, counts, p: int):
+    """The p non-empty supers of highest cosine with q, best first, lowest
+    index on ties.  Returns (probes [<= p], cos [S])."""
+    cs = cosine(np.asarray(q, np.float64)[None], SC)[0]
+    valid = np.nonzero(np.asarray(counts) > 0)[0]
+    order = valid[np.lexsort((valid, -cs[valid]))]
+    return order[:p], cs
+
+
+def lookup_probed(q, C, e2s, probes):
+    """The entry of highest cosine with q among the members of the probed
+    supers, lowest entry index on ties.  Returns (idx, candidates, their
+    cosines)."""
+    e2s = np.asarray(e2s).astype(np.int64)
+    cand = np.nonzero(np.isin(e2s, np.asarray(probes)))[0]
+    ce = cosine(np.asarray(q, np.float64)[None], np.asarray(C, np.float64)[cand])[0]
+    j = int(np.argmax(ce))  # first maximum: candidates ascend
+    return int(cand[j]), cand, ce
+
+
+def lookup_hier(q, C, SC, e2s, counts, p: int):
+    """Two-level lookup of one query: probe, then search the probed
+    members.  Returns (idx, probes)."""
+    probes, _ = probe_supers(q, SC, counts, p)
+    idx, _, _ = lookup_probed(q, C, e2s, probes)
+    return idx, probes

@@ -481,3 +481,83 @@ def test_decode_degenerate_cases():
     out, out_lse = O.decode_with_idx(q[:1], idx[:1], np.zeros_like(Abar), Lb,
                                      K_loc[:1], V_loc[:1], 0.35)
     assert np.all(np.isneginf(out_lse)) and np.all(out == 0)
+
+
+# ---------------------------------------------------------------- hierarchical lookup
+
+def _unit(deg):
+    t = math.radians(deg)
+    return np.array([math.cos(t), math.sin(t)])
+
+
+def test_hier_lookup_hand_worked_probe_miss_and_hit():
+    """Supers at 0 and 90 degrees; entries at 0 and 50 degrees belong to the
+    first, 80 and 90 degrees to the second.  A query at 60 degrees is nearer
+    the second super (cos 30 deg > cos 60 deg), so one probe searches
+    {80, 90} and returns the 80-degree entry (cos 20 deg), although the
+    50-degree entry is the flat nearest (cos 10 deg); two probes find it."""
+    C = np.stack([_unit(0), _unit(50), _unit(80), _unit(90)])
+    SC = np.stack([_unit(0), _unit(90)])
+    e2s = np.array([0, 0, 1, 1])
+    counts = np.array([2, 2])
+    q = 3.0 * _unit(60)
+    idx1, probes1 = O.lookup_hier(q, C, SC, e2s, counts, 1)
+    assert list(probes1) == [1] and idx1 == 2
+    idx2, probes2 = O.lookup_hier(q, C, SC, e2s, counts, 2)
+    assert list(probes2) == [1, 0] and idx2 == 1
+    assert O.assign(q[None], C)[0][0] == 1
+
+
+def test_hier_lookup_probing_all_supers_is_the_flat_search():
+    r = rng(8, 0)
+    for trial in range(4):
+        K, S, d = 200, 13, 16
+        C = r.standard_normal((K, d))
+        SC, e2s, counts = O.build_index(C, S, 3, "f32")
+        nonempty = int(np.sum(counts > 0))
+        Q = r.standard_normal((30, d))
+        flat = O.assign(Q, C)[0]
+        for i in range(Q.shape[0]):
+            idx, probes = O.lookup_hier(Q[i], C, SC, e2s, counts, S)
+            assert len(probes) == nonempty
+            assert idx == flat[i]
+
+
+def test_hier_lookup_one_entry_per_super_is_the_flat_search():
+    """S = K: first-K initialisation puts every entry in its own super (the
+    supers are the entries themselves), so one probe already finds the flat
+    nearest entry."""
+    r = rng(8, 1)
+    C = r.standard_normal((40, 8)).astype(np.float32).astype(np.float64)
+    SC, e2s, counts = O.build_index(C, 40, 1, "f32")
+    np.testing.assert_array_equal(e2s, np.arange(40))
+    np.testing.assert_array_equal(SC, C)
+    Q = r.standard_normal((25, 8))
+    flat = O.assign(Q, C)[0]
+    for i in range(25):
+        assert O.lookup_hier(Q[i], C, SC, e2s, counts, 1)[0] == flat[i]
+
+
+def test_hier_probes_ties_and_empty_supers():
+    """Equal super scores go to the lower index; empty supers are never
+    probed; the member search breaks ties by the lower entry index."""
+    SC = np.stack([_unit(10), _unit(10), _unit(40), _unit(10)])
+    counts = np.array([3, 0, 1, 2])
+    probes, _ = O.probe_supers(_unit(10), SC, counts, 3)
+    assert list(probes) == [0, 3, 2]
+    C = np.stack([_unit(30), _unit(20), _unit(20), _unit(80)])
+    e2s = np.array([2, 0, 3, 0])
+    idx, cand, _ = O.lookup_probed(_unit(20), C, e2s, [0, 3])
+    assert list(cand) == [1, 2, 3] and idx == 1
+
+
+def test_index_members_against_brute_force():
+    r = rng(8, 2)
+    S = 9
+    e2s = r.integers(0, S, 300)
+    e2s[e2s == 4] = 5  # an empty super
+    offsets, members = O.index_members(e2s, S)
+    for s in range(S):
+        expect = [k for k in range(300) if e2s[k] == s]
+        assert list(members[offsets[s]:offsets[s + 1]]) == expect
+    assert offsets[-1] == 300
