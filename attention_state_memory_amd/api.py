@@ -42,6 +42,14 @@ SIGNATURES = {
     "asm_aggregate_ws": (_c_size, [_c_int] * 5),
     "asm_aggregate": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int,
                                _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_size, _vp]),
+    "asm_build_index_ws": (_c_size, [_c_int] * 5),
+    "asm_build_index": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                 _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_size, _vp]),
+    "asm_decode_step_hier_ws": (_c_size, [_c_int] * 8),
+    "asm_decode_step_hier": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                      _c_float, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                      _vp, _vp, _c_i64, _c_i64, _c_i64, _vp, _vp, _c_int,
+                                      _vp, _vp, _vp, _vp, _vp, _c_size, _vp]),
 }
 
 _lib: Optional[ctypes.CDLL] = None
@@ -288,3 +296,66 @@ def build_memory(X, K: int, iters: int, A=None, LSE=None):
         _, _, _, Abar, LSEbar = aggregate(X, idx, C, A=A, LSE=LSE, cinv=cinv, count=count,
                                           with_states=last)
     return C, cinv, count, idx, Abar, LSEbar
+
+
+def build_index(C, S: int, iters: int, *, workspace=None):
+    """Two-level index over each head's entries.  C [H, K, d].  Returns
+    (SC [H, S, d], scinv [H, S], counts [H, S], offsets [H, S+1],
+    members [H, K])."""
+    _dev(C, "C")
+    code = _dtype_code(C)
+    H, K, d = C.shape
+    dev = C.device
+    SC = torch.empty((H, S, d), dtype=C.dtype, device=dev)
+    scinv = torch.empty((H, S), dtype=torch.float32, device=dev)
+    counts = torch.empty((H, S), dtype=torch.int32, device=dev)
+    offsets = torch.empty((H, S + 1), dtype=torch.int32, device=dev)
+    members = torch.empty((H, K), dtype=torch.int32, device=dev)
+    nbytes = int(lib().asm_build_index_ws(code, H, K, S, d))
+    ws = _workspace(nbytes, dev, workspace)
+    _check("asm_build_index", lib().asm_build_index(
+        code, H, K, int(S), d, int(iters), _ptr(C), _ptr(SC), _ptr(scinv), _ptr(counts),
+        _ptr(offsets), _ptr(members), _ptr(ws), nbytes, _stream(dev)))
+    return SC, scinv, counts, offsets, members
+
+
+def decode_step_hier(q, C, cinv, index, p: int, Abar, LSEbar, Kl, Vl, kv_start, kv_len,
+                     max_kv_len: int, scale: float, *, out=None, out_lse=None, out_idx=None,
+                     want_probes: bool = False, workspace=None):
+    """Decode step with the two-level lookup.  `index` is the tuple returned
+    by build_index.  Returns (out, out_lse, out_idx, probes | None)."""
+    SC, scinv, _, offsets, members = index
+    for t, n in ((q, "q"), (C, "C"), (SC, "SC"), (Kl, "Kl"), (Vl, "Vl")):
+        _dev(t, n)
+    _dev(cinv, "cinv", torch.float32)
+    _dev(scinv, "scinv", torch.float32)
+    _dev(offsets, "offsets", torch.int32)
+    _dev(members, "members", torch.int32)
+    _dev(Abar, "Abar", torch.float32)
+    _dev(LSEbar, "LSEbar", torch.float32)
+    _dev(kv_start, "kv_start", torch.int32)
+    _dev(kv_len, "kv_len", torch.int32)
+    code = _dtype_code(q)
+    if Kl.stride() != Vl.stride() or Kl.shape != Vl.shape or Kl.stride(2) != 1:
+        raise ValueError("Kl and Vl must share shape and strides, d contiguous")
+    B, Hq, d = q.shape
+    K = C.shape[1]
+    S = SC.shape[1]
+    Hkv, cap, _ = Kl.shape
+    dev = q.device
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+    if out_lse is None:
+        out_lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    if out_idx is None:
+        out_idx = torch.empty((B, Hq), dtype=torch.int32, device=dev)
+    probes = torch.empty((B, Hq, p), dtype=torch.int32, device=dev) if want_probes else None
+    nbytes = int(lib().asm_decode_step_hier_ws(code, B, Hq, Hkv, d, K, S, int(max_kv_len)))
+    ws = _workspace(nbytes, dev, workspace)
+    _check("asm_decode_step_hier", lib().asm_decode_step_hier(
+        code, B, Hq, Hkv, d, K, S, int(p), float(scale), _ptr(q), _ptr(C), _ptr(cinv), _ptr(SC),
+        _ptr(scinv), _ptr(offsets), _ptr(members), _ptr(Abar), _ptr(LSEbar), _ptr(Kl), _ptr(Vl),
+        Kl.stride(0), Kl.stride(1), cap, _ptr(kv_start), _ptr(kv_len), int(max_kv_len), _ptr(out),
+        _ptr(out_lse), _ptr(out_idx), _ptr(probes), _ptr(ws), nbytes, _stream(dev)))
+    return out, out_lse, out_idx, probes
+

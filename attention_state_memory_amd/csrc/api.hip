@@ -78,7 +78,7 @@ int check_ws(const void* ws, size_t ws_bytes, size_t need) {
 struct DecodePlan {
   bool fast = false;
   int Bc = 0;  // sequences per launch
-  int n_waves = 0, uph = 0;                     // MFMA path
+  int n_waves = 0, uph = 0, score_uph = 0;      // MFMA path
   int split_tok = 0, S_max = 0, score_tiles = 0;  // VALU path
   size_t off_keys = 0, off_tp = 0, off_pa = 0, off_pl = 0, total = 0;
 };
@@ -111,24 +111,27 @@ int decode_split_tokens(int B, int Hkv, int max_kv_len) {
   return int(s);
 }
 
+// keys_given: the argmax keys come from the hierarchical lookup (one per
+// head and sequence), so the main kernel scores nothing.
 DecodePlan plan_decode(int dtype, int B, int Hq, int Hkv, int d, int K, int max_kv_len,
-                       int64_t kv_tok_stride) {
+                       int64_t kv_tok_stride, bool keys_given = false) {
   DecodePlan p;
   const int G = Hq / Hkv;
   p.fast = asmk::decode_fast_path(dtype, d, G, kv_tok_stride, max_kv_len);
   size_t off = 0;
   if (p.fast) {
     p.Bc = B < asmk::kFastMaxBatch ? B : asmk::kFastMaxBatch;
-    p.uph = (K + 63) / 64;
+    p.uph = keys_given ? 1 : (K + 63) / 64;
+    p.score_uph = keys_given ? 0 : p.uph;
     // Persistent grid: as many waves as fit on the device at once, but no
     // more than one per work unit (16 KB each): small steps are latency-bound
     // and gain from spreading their few units over many waves.
-    const int64_t units = int64_t(Hq) * p.uph + int64_t(p.Bc) * Hkv * ((int64_t(max_kv_len) + 31) / 32);
+    const int64_t units = int64_t(Hq) * p.score_uph + int64_t(p.Bc) * Hkv * ((int64_t(max_kv_len) + 31) / 32);
     const int64_t cap = int64_t(device_cus()) * asmk::decode_fast_waves_per_cu(d, G);
     int64_t w = units;
     w = env_int("ASM_DECODE_WAVES", int(w < cap ? w : cap));
+    if (w < 1) w = 1;
     w = (w + 3) / 4 * 4;
-    if (w < 4) w = 4;
     p.n_waves = int(w);
     p.off_keys = off;
     off = asmk::align_up(off + size_t(Hq) * p.Bc * p.uph * sizeof(uint64_t), kAlign);
@@ -165,6 +168,76 @@ int validate_decode_shape(int dtype, int B, int Hq, int Hkv, int d, int K, int m
   const int64_t items = int64_t(B) * Hkv * ((int64_t(max_kv_len) + 127) / 128) + int64_t(Hq) * ((K + 255) / 256);
   if (items > (int64_t(1) << 30) || int64_t(B) * Hq > (int64_t(1) << 30))
     return fail(ASM_ERR_SHAPE, "decode problem too large for one launch");
+  return ASM_OK;
+}
+
+// The decode step for both lookups; `hier` (hierarchical lookup) is NULL for
+// the flat search.
+int decode_impl(int dtype, int B, int Hq, int Hkv, int d, int K, float scale,
+                const void* q, const void* C, const float* cinv, const float* Abar,
+                const float* LSEbar, const void* Kl, const void* Vl,
+                int64_t kv_head_stride, int64_t kv_tok_stride, int64_t kv_capacity,
+                const int32_t* kv_start, const int32_t* kv_len, int max_kv_len,
+                float* out, float* out_lse, int32_t* out_idx,
+                void* ws, size_t ws_bytes, hipStream_t stream, asmk::HierArgs* hier) {
+  ASM_TRY(validate_decode_shape(dtype, B, Hq, Hkv, d, K, max_kv_len));
+  if (!(scale == scale) || scale == INFINITY || scale == -INFINITY)
+    return fail(ASM_ERR_SHAPE, "scale must be finite");
+  if (!q || !C || !cinv || !Abar || !LSEbar || !kv_start || !kv_len || !out)
+    return fail(ASM_ERR_NULL, "q, C, cinv, Abar, LSEbar, kv_start, kv_len and out are required");
+  if (max_kv_len > 0) {
+    if (!Kl || !Vl) return fail(ASM_ERR_NULL, "Kl and Vl are required when max_kv_len > 0");
+    if (kv_head_stride < 0 || kv_tok_stride < 1 || kv_capacity < 0)
+      return fail(ASM_ERR_SHAPE, "need kv_head_stride >= 0, kv_tok_stride >= 1, kv_capacity >= 0");
+    if (dtype == ASM_BF16 && (kv_head_stride % 8 != 0 || kv_tok_stride % 8 != 0))
+      return fail(ASM_ERR_ALIGN, "bf16 kv strides must be multiples of 8 elements");
+  }
+  ASM_TRY(check_bf16_ptrs(dtype, {q, C, Kl, Vl}));
+  const DecodePlan p = plan_decode(dtype, B, Hq, Hkv, d, K, max_kv_len, kv_tok_stride, hier != nullptr);
+  if (hier != nullptr && !p.fast)
+    return fail(ASM_ERR_SHAPE,
+                "the hierarchical lookup needs bf16, d in {64, 128}, Hq/Hkv in {1, 2, 4, 8} "
+                "and local KV rows of under 2 GiB per sequence");
+  ASM_TRY(check_ws(ws, ws_bytes, p.total));
+
+  asmk::DecodeArgs a{};
+  a.Hq = Hq; a.Hkv = Hkv; a.d = d; a.K = K;
+  a.scale2 = scale * ASM_LOG2E;
+  a.C = C; a.cinv = cinv; a.Abar = Abar; a.LSEbar = LSEbar;
+  a.Kl = Kl; a.Vl = Vl;
+  a.kv_head_stride = kv_head_stride; a.kv_tok_stride = kv_tok_stride; a.kv_capacity = kv_capacity;
+  a.max_kv_len = max_kv_len;
+  a.n_waves = p.n_waves; a.uph = p.uph; a.score_uph = p.score_uph;
+  a.split_tok = p.split_tok; a.S_max = p.S_max; a.score_tiles = p.score_tiles;
+  char* w = static_cast<char*>(ws);
+  a.keys = reinterpret_cast<uint64_t*>(w + p.off_keys);
+  a.tile_prefix = reinterpret_cast<int32_t*>(w + p.off_tp);
+  a.part_a = reinterpret_cast<float*>(w + p.off_pa);
+  a.part_lse = reinterpret_cast<float*>(w + p.off_pl);
+  const size_t esz = dtype == ASM_BF16 ? 2 : 4;
+  int32_t* probes_base = hier ? hier->probes_out : nullptr;
+  // Sequences are independent: batches larger than one launch's limit run
+  // as consecutive launches over batch slices sharing the workspace.
+  for (int b0 = 0; b0 < B; b0 += p.Bc) {
+    const int nb = B - b0 < p.Bc ? B - b0 : p.Bc;
+    a.B = nb;
+    a.q = static_cast<const char*>(q) + size_t(b0) * Hq * d * esz;
+    a.kv_start = kv_start + b0;
+    a.kv_len = kv_len + b0;
+    a.out = out + size_t(b0) * Hq * d;
+    a.out_lse = out_lse ? out_lse + size_t(b0) * Hq : nullptr;
+    a.out_idx = out_idx ? out_idx + size_t(b0) * Hq : nullptr;
+    if (hier != nullptr) {
+      hier->B = nb;
+      hier->q = a.q;
+      hier->keys = a.keys;
+      hier->probes_out = probes_base ? probes_base + size_t(b0) * Hq * hier->p : nullptr;
+      const int sth = hip_status(asmk::launch_hier_lookup(*hier, stream), "decode_step_hier");
+      if (sth != ASM_OK) return sth;
+    }
+    const int st = hip_status(asmk::launch_decode(a, dtype, stream), "decode_step");
+    if (st != ASM_OK) return st;
+  }
   return ASM_OK;
 }
 
@@ -219,52 +292,43 @@ int asm_decode_step(int dtype, int B, int Hq, int Hkv, int d, int K, float scale
                     const int32_t* kv_start, const int32_t* kv_len, int max_kv_len,
                     float* out, float* out_lse, int32_t* out_idx,
                     void* ws, size_t ws_bytes, hipStream_t stream) {
-  ASM_TRY(validate_decode_shape(dtype, B, Hq, Hkv, d, K, max_kv_len));
-  if (!(scale == scale) || scale == INFINITY || scale == -INFINITY)
-    return fail(ASM_ERR_SHAPE, "scale must be finite");
-  if (!q || !C || !cinv || !Abar || !LSEbar || !kv_start || !kv_len || !out)
-    return fail(ASM_ERR_NULL, "q, C, cinv, Abar, LSEbar, kv_start, kv_len and out are required");
-  if (max_kv_len > 0) {
-    if (!Kl || !Vl) return fail(ASM_ERR_NULL, "Kl and Vl are required when max_kv_len > 0");
-    if (kv_head_stride < 0 || kv_tok_stride < 1 || kv_capacity < 0)
-      return fail(ASM_ERR_SHAPE, "need kv_head_stride >= 0, kv_tok_stride >= 1, kv_capacity >= 0");
-    if (dtype == ASM_BF16 && (kv_head_stride % 8 != 0 || kv_tok_stride % 8 != 0))
-      return fail(ASM_ERR_ALIGN, "bf16 kv strides must be multiples of 8 elements");
-  }
-  ASM_TRY(check_bf16_ptrs(dtype, {q, C, Kl, Vl}));
-  const DecodePlan p = plan_decode(dtype, B, Hq, Hkv, d, K, max_kv_len, kv_tok_stride);
-  ASM_TRY(check_ws(ws, ws_bytes, p.total));
+  return decode_impl(dtype, B, Hq, Hkv, d, K, scale, q, C, cinv, Abar, LSEbar, Kl, Vl,
+                     kv_head_stride, kv_tok_stride, kv_capacity, kv_start, kv_len, max_kv_len,
+                     out, out_lse, out_idx, ws, ws_bytes, stream, nullptr);
+}
 
-  asmk::DecodeArgs a{};
-  a.Hq = Hq; a.Hkv = Hkv; a.d = d; a.K = K;
-  a.scale2 = scale * ASM_LOG2E;
-  a.C = C; a.cinv = cinv; a.Abar = Abar; a.LSEbar = LSEbar;
-  a.Kl = Kl; a.Vl = Vl;
-  a.kv_head_stride = kv_head_stride; a.kv_tok_stride = kv_tok_stride; a.kv_capacity = kv_capacity;
-  a.max_kv_len = max_kv_len;
-  a.n_waves = p.n_waves; a.uph = p.uph;
-  a.split_tok = p.split_tok; a.S_max = p.S_max; a.score_tiles = p.score_tiles;
-  char* w = static_cast<char*>(ws);
-  a.keys = reinterpret_cast<uint64_t*>(w + p.off_keys);
-  a.tile_prefix = reinterpret_cast<int32_t*>(w + p.off_tp);
-  a.part_a = reinterpret_cast<float*>(w + p.off_pa);
-  a.part_lse = reinterpret_cast<float*>(w + p.off_pl);
-  const size_t esz = dtype == ASM_BF16 ? 2 : 4;
-  // Sequences are independent: batches larger than one launch's limit run
-  // as consecutive launches over batch slices sharing the workspace.
-  for (int b0 = 0; b0 < B; b0 += p.Bc) {
-    const int nb = B - b0 < p.Bc ? B - b0 : p.Bc;
-    a.B = nb;
-    a.q = static_cast<const char*>(q) + size_t(b0) * Hq * d * esz;
-    a.kv_start = kv_start + b0;
-    a.kv_len = kv_len + b0;
-    a.out = out + size_t(b0) * Hq * d;
-    a.out_lse = out_lse ? out_lse + size_t(b0) * Hq : nullptr;
-    a.out_idx = out_idx ? out_idx + size_t(b0) * Hq : nullptr;
-    const int st = hip_status(asmk::launch_decode(a, dtype, stream), "decode_step");
-    if (st != ASM_OK) return st;
-  }
-  return ASM_OK;
+size_t asm_decode_step_hier_ws(int dtype, int B, int Hq, int Hkv, int d, int K, int S,
+                               int max_kv_len) {
+  if (validate_decode_shape(dtype, B, Hq, Hkv, d, K, max_kv_len) != ASM_OK) return 0;
+  if (S < 1 || S > K) return 0;
+  return plan_decode(dtype, B, Hq, Hkv, d, K, max_kv_len, d, true).total;
+}
+
+int asm_decode_step_hier(int dtype, int B, int Hq, int Hkv, int d, int K, int S, int p,
+                         float scale, const void* q, const void* C, const float* cinv,
+                         const void* SC, const float* scinv, const int32_t* offsets,
+                         const int32_t* members, const float* Abar, const float* LSEbar,
+                         const void* Kl, const void* Vl, int64_t kv_head_stride,
+                         int64_t kv_tok_stride, int64_t kv_capacity, const int32_t* kv_start,
+                         const int32_t* kv_len, int max_kv_len, float* out, float* out_lse,
+                         int32_t* out_idx, int32_t* out_probes, void* ws, size_t ws_bytes,
+                         hipStream_t stream) {
+  ASM_TRY(check_dtype(dtype));
+  if (!asmk::hier_fast_path(dtype, d))
+    return fail(ASM_ERR_SHAPE, "the hierarchical lookup needs bf16 and d in {64, 128}");
+  if (S < 1 || S > K || S > asmk::kHierMaxSupers)
+    return fail(ASM_ERR_SHAPE, "need 1 <= S <= min(K, %d) (S=%d, K=%d)", asmk::kHierMaxSupers, S, K);
+  if (p < 1 || p > asmk::kHierMaxProbes)
+    return fail(ASM_ERR_SHAPE, "need 1 <= p <= %d (p=%d)", asmk::kHierMaxProbes, p);
+  if (!SC || !scinv || !offsets || !members) return fail(ASM_ERR_NULL, "SC, scinv, offsets and members are required");
+  ASM_TRY(check_bf16_ptrs(dtype, {SC}));
+  asmk::HierArgs h{};
+  h.Hq = Hq; h.K = K; h.S = S; h.d = d; h.p = p;
+  h.C = C; h.cinv = cinv; h.SC = SC; h.scinv = scinv; h.offsets = offsets; h.members = members;
+  h.probes_out = out_probes;
+  return decode_impl(dtype, B, Hq, Hkv, d, K, scale, q, C, cinv, Abar, LSEbar, Kl, Vl,
+                     kv_head_stride, kv_tok_stride, kv_capacity, kv_start, kv_len, max_kv_len,
+                     out, out_lse, out_idx, ws, ws_bytes, stream, &h);
 }
 
 // ---------------------------------------------------------------------------
@@ -373,6 +437,60 @@ int asm_aggregate(int dtype, int H, int N, int K, int d, const void* X, const in
   off += asmk::align_up(size_t(H) * K * sizeof(int32_t), kAlign);
   a.perm = reinterpret_cast<int32_t*>(w + off);
   return hip_status(asmk::launch_aggregate(a, dtype, stream), "aggregate");
+}
+
+// ---------------------------------------------------------------------------
+static size_t build_index_ws_bytes(int H, int K, int S) {
+  size_t off = asmk::align_up(size_t(H) * K * sizeof(int32_t), kAlign);  // entry -> super
+  off += asmk::align_up(size_t(H) * S * sizeof(int32_t), kAlign);        // scatter cursors
+  return off;
+}
+
+size_t asm_build_index_ws(int dtype, int H, int K, int S, int d) {
+  if (check_dtype(dtype) != ASM_OK || check_d(dtype, d) != ASM_OK || H < 0 || K < 1 || S < 1 || S > K)
+    return 0;
+  return build_index_ws_bytes(H, K, S);
+}
+
+int asm_build_index(int dtype, int H, int K, int S, int d, int iters, const void* C, void* SC,
+                    float* scinv, int32_t* counts, int32_t* offsets, int32_t* members, void* ws,
+                    size_t ws_bytes, hipStream_t stream) {
+  ASM_TRY(check_dtype(dtype));
+  ASM_TRY(check_d(dtype, d));
+  if (H < 0 || K < 1 || S < 1 || S > K || iters < 1)
+    return fail(ASM_ERR_SHAPE, "need H >= 0, 1 <= S <= K and iters >= 1 (S=%d K=%d iters=%d)", S, K, iters);
+  if (int64_t(H) * K > (int64_t(1) << 30)) return fail(ASM_ERR_SHAPE, "H*K too large");
+  if (H == 0) return ok();
+  if (!C || !SC || !scinv || !counts || !offsets || !members)
+    return fail(ASM_ERR_NULL, "C, SC, scinv, counts, offsets and members are required");
+  ASM_TRY(check_bf16_ptrs(dtype, {C, SC}));
+  ASM_TRY(check_ws(ws, ws_bytes, build_index_ws_bytes(H, K, S)));
+  char* w = static_cast<char*>(ws);
+  int32_t* e2s = reinterpret_cast<int32_t*>(w);
+  int32_t* cursor = reinterpret_cast<int32_t*>(w + asmk::align_up(size_t(H) * K * sizeof(int32_t), kAlign));
+  const size_t esz = dtype == ASM_BF16 ? 2 : 4;
+  // first-S initialisation: the first S entries of every head
+  int st = hip_status(hipMemcpy2DAsync(SC, size_t(S) * d * esz, C, size_t(K) * d * esz,
+                                       size_t(S) * d * esz, size_t(H), hipMemcpyDeviceToDevice, stream),
+                      "build_index");
+  if (st != ASM_OK) return st;
+  st = hip_status(asmk::launch_inv_norms(dtype, H, S, d, SC, scinv, stream), "build_index");
+  if (st != ASM_OK) return st;
+  for (int it = 0; it < iters; ++it) {
+    asmk::AssignArgs as{};
+    as.H = H; as.N = K; as.K = S; as.d = d;
+    as.X = C; as.C = SC; as.cinv = scinv; as.idx = e2s; as.best = nullptr;
+    st = hip_status(asmk::launch_assign(as, dtype, stream), "build_index");
+    if (st != ASM_OK) return st;
+    // mean step; its counting sort leaves the member lists of this partition
+    asmk::AggregateArgs ag{};
+    ag.H = H; ag.N = K; ag.K = S; ag.d = d;
+    ag.X = C; ag.idx = e2s; ag.C = SC; ag.cinv = scinv; ag.count = counts;
+    ag.offsets = offsets; ag.cursor = cursor; ag.perm = members;
+    st = hip_status(asmk::launch_aggregate(ag, dtype, stream), "build_index");
+    if (st != ASM_OK) return st;
+  }
+  return ASM_OK;
 }
 
 }  // extern "C"

@@ -427,7 +427,7 @@ decode_fast_main(DecodeArgs a) {
 
   const int64_t gw = int64_t(blockIdx.x) * 4 + w;
   const int64_t W = a.n_waves;
-  const int64_t SU = int64_t(a.Hq) * a.uph;
+  const int64_t SU = int64_t(a.Hq) * a.score_uph;
   const int64_t U = int64_t(__builtin_amdgcn_readfirstlane(tp[a.B])) * a.Hkv;
 
   // scoring share first: every wave scores at the same time, so the table

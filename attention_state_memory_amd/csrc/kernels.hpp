@@ -33,7 +33,9 @@ struct DecodeArgs {
   int32_t* out_idx;
   // MFMA path
   int n_waves;           // persistent waves (multiple of 4)
-  int uph;               // scoring units per head = ceil(K / 64)
+  int uph;               // argmax keys per (head, sequence): ceil(K / 64) units
+  int score_uph;         // units per head the main kernel scores: uph, or 0 when
+                         // the keys were written beforehand (hierarchical lookup)
   int32_t* tile_prefix;  // [B + 1] 32-token tiles per kv head, prefix over sequences
   // VALU path
   int split_tok;    // local tokens per attention item
@@ -50,6 +52,24 @@ bool decode_fast_path(int dtype, int d, int G, int64_t kv_tok_stride, int max_kv
 int decode_fast_waves_per_cu(int d, int G);  // resident waves per CU of the MFMA main kernel
 hipError_t launch_decode_fast(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t s);
+
+// ---- hierarchical lookup ------------------------------------------------------
+constexpr int kHierMaxProbes = 32;
+constexpr int kHierMaxSupers = 1024;
+struct HierArgs {
+  int B, Hq, K, S, d, p;
+  const void* q;        // [B, Hq, d]
+  const void* C;        // [Hq, K, d]
+  const float* cinv;    // [Hq, K]
+  const void* SC;       // [Hq, S, d] super-centroids
+  const float* scinv;   // [Hq, S]
+  const int32_t* offsets;  // [Hq, S + 1]
+  const int32_t* members;  // [Hq, K]
+  uint64_t* keys;       // [Hq, B] one argmax key per (head, sequence)
+  int32_t* probes_out;  // [B, Hq, p] nullable
+};
+bool hier_fast_path(int dtype, int d);
+hipError_t launch_hier_lookup(const HierArgs& a, hipStream_t s);
 
 // ---- centroid inverse norms -------------------------------------------------
 hipError_t launch_inv_norms(int dtype, int H, int K, int d, const void* C, float* cinv,

@@ -60,7 +60,7 @@ enum asm_status_code {
 enum asm_dtype { ASM_BF16 = 0, ASM_F32 = 1 };
 
 /* ABI version of this header (bumped on any signature change). */
-#define ASM_ABI_VERSION 1
+#define ASM_ABI_VERSION 2
 int asm_abi_version(void);
 
 /* Static text for a status code. */
@@ -118,6 +118,37 @@ int asm_decode_step(int dtype, int B, int Hq, int Hkv, int d, int K, float scale
                     const int32_t* kv_start, const int32_t* kv_len, int max_kv_len,
                     float* out, float* out_lse, int32_t* out_idx,
                     void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * asm_decode_step_hier -- the decode step with the two-level lookup of an
+ * index built by asm_build_index ([TS] Complejidad: the lookup grows with
+ * the logarithm of the memory size through a hierarchical index; two levels
+ * are used).  Per (b, h): the S super-centroids of head h are scored as in
+ * step 1 of asm_decode_step (q.SC * scinv); the p best supers with members
+ * are probed (lowest index on exact ties); idx[b,h] is the member entry k of
+ * a probed super maximising q.C[h,k] * cinv[h,k] (lowest k on exact ties).
+ * Steps 2-4 of asm_decode_step follow unchanged.  With p >= the number of
+ * non-empty supers this is the flat search.
+ *   bf16, d in {64, 128}, Hq/Hkv in {1, 2, 4, 8}; 1 <= S <= min(K, 1024);
+ *   1 <= p <= 32.
+ *   SC [Hq, S, d] bf16; scinv [Hq, S]; offsets [Hq, S+1]; members [Hq, K]
+ *   int32: as written by asm_build_index.
+ *   out_probes [B, Hq, p] int32 (nullable): the probed supers, best first,
+ *   -1 past the number of non-empty supers.
+ *   Other arguments as asm_decode_step; the workspace size comes from
+ *   asm_decode_step_hier_ws.
+ */
+size_t asm_decode_step_hier_ws(int dtype, int B, int Hq, int Hkv, int d, int K, int S,
+                               int max_kv_len);
+int asm_decode_step_hier(int dtype, int B, int Hq, int Hkv, int d, int K, int S, int p,
+                         float scale, const void* q, const void* C, const float* cinv,
+                         const void* SC, const float* scinv, const int32_t* offsets,
+                         const int32_t* members, const float* Abar, const float* LSEbar,
+                         const void* Kl, const void* Vl, int64_t kv_head_stride,
+                         int64_t kv_tok_stride, int64_t kv_capacity, const int32_t* kv_start,
+                         const int32_t* kv_len, int max_kv_len, float* out, float* out_lse,
+                         int32_t* out_idx, int32_t* out_probes, void* ws, size_t ws_bytes,
+                         hipStream_t stream);
 
 /*
  * asm_build_states -- prefix attention states of the calibration queries
@@ -180,6 +211,25 @@ size_t asm_aggregate_ws(int dtype, int H, int N, int K, int d);
 int asm_aggregate(int dtype, int H, int N, int K, int d, const void* X, const int32_t* idx,
                   const float* A, const float* LSE, void* C, float* cinv, int32_t* count,
                   float* Abar, float* LSEbar, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * asm_build_index -- the two-level index used by asm_decode_step_hier.  For
+ * every head the K entry queries C[h] are clustered into S super-centroids
+ * with the build's cosine k-means (asm_kmeans_assign and the mean step of
+ * asm_aggregate): first-S initialisation (SC[h] = C[h, :S]), then `iters`
+ * rounds of assignment and mean.  The partition is the last assignment,
+ * whose means are SC.
+ *   C [H, K, d] dtype; 1 <= S <= K; iters >= 1.
+ *   Outputs: SC [H, S, d] dtype; scinv [H, S] float32 (1/|SC|, 0 for a zero
+ *   row); counts [H, S] int32; offsets [H, S+1] int32 (exclusive prefix of
+ *   counts per head); members [H, K] int32: the entries of super s are
+ *   members[h, offsets[h,s] .. offsets[h,s+1]), in unspecified order.
+ *   Workspace: asm_build_index_ws bytes.
+ */
+size_t asm_build_index_ws(int dtype, int H, int K, int S, int d);
+int asm_build_index(int dtype, int H, int K, int S, int d, int iters, const void* C, void* SC,
+                    float* scinv, int32_t* counts, int32_t* offsets, int32_t* members, void* ws,
+                    size_t ws_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }
