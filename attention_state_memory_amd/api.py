@@ -45,7 +45,7 @@ SIGNATURES = {
     "asm_build_index_ws": (_c_size, [_c_int] * 5),
     "asm_build_index": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                  _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_size, _vp]),
-    "asm_decode_step_hier_ws": (_c_size, [_c_int] * 8),
+    "asm_decode_step_hier_ws": (_c_size, [_c_int] * 9),
     "asm_decode_step_hier": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                       _c_float, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                       _vp, _vp, _c_i64, _c_i64, _c_i64, _vp, _vp, _c_int,
@@ -350,7 +350,7 @@ def decode_step_hier(q, C, cinv, index, p: int, Abar, LSEbar, Kl, Vl, kv_start, 
     if out_idx is None:
         out_idx = torch.empty((B, Hq), dtype=torch.int32, device=dev)
     probes = torch.empty((B, Hq, p), dtype=torch.int32, device=dev) if want_probes else None
-    nbytes = int(lib().asm_decode_step_hier_ws(code, B, Hq, Hkv, d, K, S, int(max_kv_len)))
+    nbytes = int(lib().asm_decode_step_hier_ws(code, B, Hq, Hkv, d, K, S, int(p), int(max_kv_len)))
     ws = _workspace(nbytes, dev, workspace)
     _check("asm_decode_step_hier", lib().asm_decode_step_hier(
         code, B, Hq, Hkv, d, K, S, int(p), float(scale), _ptr(q), _ptr(C), _ptr(cinv), _ptr(SC),

@@ -111,18 +111,18 @@ int decode_split_tokens(int B, int Hkv, int max_kv_len) {
   return int(s);
 }
 
-// keys_given: the argmax keys come from the hierarchical lookup (one per
-// head and sequence), so the main kernel scores nothing.
+// keys_given > 0: that many argmax keys per (head, sequence) come from the
+// two-level lookup (one per probe), so the main kernel scores nothing.
 DecodePlan plan_decode(int dtype, int B, int Hq, int Hkv, int d, int K, int max_kv_len,
-                       int64_t kv_tok_stride, bool keys_given = false) {
+                       int64_t kv_tok_stride, int keys_given = 0) {
   DecodePlan p;
   const int G = Hq / Hkv;
   p.fast = asmk::decode_fast_path(dtype, d, G, kv_tok_stride, max_kv_len);
   size_t off = 0;
   if (p.fast) {
     p.Bc = B < asmk::kFastMaxBatch ? B : asmk::kFastMaxBatch;
-    p.uph = keys_given ? 1 : (K + 63) / 64;
-    p.score_uph = keys_given ? 0 : p.uph;
+    p.uph = keys_given > 0 ? keys_given : (K + 63) / 64;
+    p.score_uph = keys_given > 0 ? 0 : p.uph;
     // Persistent grid: as many waves as fit on the device at once, but no
     // more than one per work unit (16 KB each): small steps are latency-bound
     // and gain from spreading their few units over many waves.
@@ -193,7 +193,8 @@ int decode_impl(int dtype, int B, int Hq, int Hkv, int d, int K, float scale,
       return fail(ASM_ERR_ALIGN, "bf16 kv strides must be multiples of 8 elements");
   }
   ASM_TRY(check_bf16_ptrs(dtype, {q, C, Kl, Vl}));
-  const DecodePlan p = plan_decode(dtype, B, Hq, Hkv, d, K, max_kv_len, kv_tok_stride, hier != nullptr);
+  const DecodePlan p = plan_decode(dtype, B, Hq, Hkv, d, K, max_kv_len, kv_tok_stride,
+                                   hier != nullptr ? hier->p : 0);
   if (hier != nullptr && !p.fast)
     return fail(ASM_ERR_SHAPE,
                 "the hierarchical lookup needs bf16, d in {64, 128}, Hq/Hkv in {1, 2, 4, 8} "
@@ -297,11 +298,11 @@ int asm_decode_step(int dtype, int B, int Hq, int Hkv, int d, int K, float scale
                      out, out_lse, out_idx, ws, ws_bytes, stream, nullptr);
 }
 
-size_t asm_decode_step_hier_ws(int dtype, int B, int Hq, int Hkv, int d, int K, int S,
+size_t asm_decode_step_hier_ws(int dtype, int B, int Hq, int Hkv, int d, int K, int S, int p,
                                int max_kv_len) {
   if (validate_decode_shape(dtype, B, Hq, Hkv, d, K, max_kv_len) != ASM_OK) return 0;
-  if (S < 1 || S > K) return 0;
-  return plan_decode(dtype, B, Hq, Hkv, d, K, max_kv_len, d, true).total;
+  if (S < 1 || S > K || p < 1 || p > asmk::kHierMaxProbes) return 0;
+  return plan_decode(dtype, B, Hq, Hkv, d, K, max_kv_len, d, p).total;
 }
 
 int asm_decode_step_hier(int dtype, int B, int Hq, int Hkv, int d, int K, int S, int p,

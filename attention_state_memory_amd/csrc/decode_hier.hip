@@ -9,18 +9,19 @@
 // non-empty ones and takes the entry of highest cosine among their members;
 // probing every super is the flat search.
 //
-// One workgroup per (sequence, query head):
+// One workgroup per (sequence, query head, probe rank r), r < p:
 //   1. the query goes to LDS as float32;
 //   2. each thread scores up to four supers (a dot product over its 16-byte
-//      row pieces against the query in LDS) into (score, index) keys; empty
-//      supers get no key;
-//   3. p rounds of a block-wide maximum pick the probes (lowest index on
-//      exact ties);
-//   4. the members of the probes are scored in one flattened loop and the
-//      block-wide maximum key, the entry of highest score and lowest index,
-//      is written where the flat search writes its unit keys (one unit per
-//      head), so the attention and merge kernels of the flat path follow
-//      unchanged.
+//      row pieces against the query in LDS) into (score, index) keys, kept
+//      in LDS; empty supers get no key;
+//   3. each thread counts, for its supers, how many keys are larger: the
+//      super of rank r is this workgroup's probe (ranks are unique: keys
+//      carry the index, lowest index first on exact score ties);
+//   4. the probe's members are scored and the block-wide maximum key, the
+//      member of highest score and lowest index, is written as unit r of
+//      (head, sequence) where the flat search writes its unit keys.  The
+//      flat path's merge kernel reduces the p units to the entry, and its
+//      attention kernel runs unchanged with scoring switched off.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -63,16 +64,17 @@ __device__ __forceinline__ uint64_t block_max_u64(uint64_t v, uint64_t* red) {
 template <int D>
 __global__ void __launch_bounds__(kThreads) hier_lookup_kernel(HierArgs a) {
   __shared__ float qs[D];
+  __shared__ uint64_t keys_s[kHierMaxSupers];
   __shared__ uint64_t red[4];
-  __shared__ int32_t probe[kHierMaxProbes];
-  __shared__ int32_t pbeg[kHierMaxProbes + 1];
-  __shared__ int32_t poff[kHierMaxProbes];
+  __shared__ int32_t probe_s;
   const int t = threadIdx.x;
-  const int item = blockIdx.x;  // b * Hq + h
+  const int r = blockIdx.x % a.p;        // probe rank of this workgroup
+  const int item = blockIdx.x / a.p;     // b * Hq + h
   const int b = item / a.Hq, h = item % a.Hq;
 
   const uint16_t* qp = static_cast<const uint16_t*>(a.q) + size_t(item) * D;
   if (t < D) qs[t] = load_elem(qp, t);
+  if (t == 0) probe_s = -1;
   __syncthreads();
 
   const uint16_t* SC = static_cast<const uint16_t*>(a.SC) + size_t(h) * a.S * D;
@@ -85,56 +87,42 @@ __global__ void __launch_bounds__(kThreads) hier_lookup_kernel(HierArgs a) {
     sk[i] = 0ull;
     if (s < a.S && off[s + 1] > off[s])
       sk[i] = argmax_key(dot_row<D>(SC + size_t(s) * D, qs) * scinv[s], uint32_t(s));
-  }
-
-  // probes: p rounds of the block-wide maximum; the owner drops the winner
-  int np = 0;
-  for (int r = 0; r < a.p; ++r) {
-    uint64_t m = sk[0];
-#pragma unroll
-    for (int i = 1; i < kSupersPerThread; ++i) m = umax64(m, sk[i]);
-    const uint64_t best = block_max_u64(m, red);
-    if (best == 0ull) break;  // no non-empty super left
-#pragma unroll
-    for (int i = 0; i < kSupersPerThread; ++i)
-      if (sk[i] == best) sk[i] = 0ull;
-    if (t == 0) probe[r] = int32_t(key_index(best));
-    np = r + 1;
-  }
-  if (t == 0) {
-    int acc = 0;
-    for (int r = 0; r < np; ++r) {
-      const int s = probe[r];
-      poff[r] = off[s];
-      pbeg[r] = acc;
-      acc += off[s + 1] - off[s];
-    }
-    pbeg[np] = acc;
+    if (s < a.S) keys_s[s] = sk[i];
   }
   __syncthreads();
+  // rank of each of this thread's supers among the non-empty ones
+#pragma unroll
+  for (int i = 0; i < kSupersPerThread; ++i) {
+    if (sk[i] == 0ull) continue;
+    int rank = 0;
+    for (int s2 = 0; s2 < a.S; ++s2) rank += keys_s[s2] > sk[i] ? 1 : 0;
+    if (rank == r) probe_s = int32_t(key_index(sk[i]));
+  }
+  __syncthreads();
+  const int probe = probe_s;
 
-  // the probed supers' members, flattened over the probes
-  const uint16_t* C = static_cast<const uint16_t*>(a.C) + size_t(h) * a.K * D;
-  const float* cinv = a.cinv + size_t(h) * a.K;
-  const int32_t* mem = a.members + size_t(h) * a.K;
-  const int total = pbeg[np];
   uint64_t best = 0ull;
-  for (int j = t; j < total; j += kThreads) {
-    int r = 0;
-    while (pbeg[r + 1] <= j) ++r;
-    const int e = mem[poff[r] + (j - pbeg[r])];
-    best = umax64(best, argmax_key(dot_row<D>(C + size_t(e) * D, qs) * cinv[e], uint32_t(e)));
+  if (probe >= 0) {
+    const uint16_t* C = static_cast<const uint16_t*>(a.C) + size_t(h) * a.K * D;
+    const float* cinv = a.cinv + size_t(h) * a.K;
+    const int32_t* mem = a.members + size_t(h) * a.K + off[probe];
+    const int n = off[probe + 1] - off[probe];
+    for (int j = t; j < n; j += kThreads) {
+      const int e = mem[j];
+      best = umax64(best, argmax_key(dot_row<D>(C + size_t(e) * D, qs) * cinv[e], uint32_t(e)));
+    }
   }
   best = block_max_u64(best, red);
-  if (t == 0) a.keys[size_t(h) * a.B + b] = best;
-  if (a.probes_out != nullptr && t < a.p)
-    a.probes_out[size_t(item) * a.p + t] = t < np ? probe[t] : -1;
+  if (t == 0) {
+    a.keys[(size_t(h) * a.B + b) * a.p + r] = best;
+    if (a.probes_out != nullptr) a.probes_out[size_t(item) * a.p + r] = probe;
+  }
 }
 
 bool hier_fast_path(int dtype, int d) { return dtype == 0 && (d == 64 || d == 128); }
 
 hipError_t launch_hier_lookup(const HierArgs& a, hipStream_t s) {
-  const dim3 grid(unsigned(a.B * a.Hq));
+  const dim3 grid(unsigned(a.B * a.Hq * a.p));
   if (a.d == 128)
     hipLaunchKernelGGL(hier_lookup_kernel<128>, grid, dim3(kThreads), 0, s, a);
   else

@@ -65,7 +65,7 @@ struct HierArgs {
   const float* scinv;   // [Hq, S]
   const int32_t* offsets;  // [Hq, S + 1]
   const int32_t* members;  // [Hq, K]
-  uint64_t* keys;       // [Hq, B] one argmax key per (head, sequence)
+  uint64_t* keys;       // [Hq, B, p] one argmax key per (head, sequence, probe)
   int32_t* probes_out;  // [B, Hq, p] nullable
 };
 bool hier_fast_path(int dtype, int d);

@@ -36,6 +36,11 @@ def to_bf16_bits(x) -> np.ndarray:
     return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
 
 
+def bf16_bits_to_float(bits) -> np.ndarray:
+    """uint16 bf16 bit patterns -> float32 (exact)."""
+    return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
 def softmax_scale(d: int) -> float:
     """The attention scale both sides use: float32(1/sqrt(d)) as a Python
     float (exactly representable in float32)."""

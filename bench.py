@@ -102,7 +102,8 @@ def parse():
                    help="run one plain device copy (256 MiB read, 256 MiB written) before the "
                         "timed region, as the reference kernel for HBM byte counters")
     p.add_argument("--workload", default="batched_decode",
-                   choices=("batched_decode", "layer_decode", "prefix_states", "memory_build"),
+                   choices=("batched_decode", "layer_decode", "layer_decode_hier", "prefix_states",
+                            "memory_build"),
                    help="batched_decode (the headline metric) or one of the offline build "
                         "workloads, reported on their MFMA rooflines")
     return p.parse_args()
@@ -116,6 +117,9 @@ def main():
         sys.exit(2)
     if args.workload == "layer_decode":
         run_layers(args)
+        return
+    if args.workload == "layer_decode_hier":
+        run_layers_hier(args)
         return
     if args.workload != "batched_decode":
         run_build(args)
@@ -364,6 +368,120 @@ def run_layers(args):
                      "algorithmic_bytes_per_step": alg,
                      "timed": "HIP events around replays of one graph holding the 32 layers' "
                               "asm_decode_step calls"},
+    }
+    print(json.dumps(result), flush=True)
+
+
+# --------------------------------------------------------------------------
+# batch-1 decode through 32 layers at K=8192: two-level lookup against flat
+# --------------------------------------------------------------------------
+
+def run_layers_hier(args, S=128, p=8, layers=32):
+    """Batch-1 decode through 32 layers with K=8192 entries per query head,
+    once with the flat search and once with the two-level lookup (S=128
+    supers, p=8 probes).  The entries are clusterable (64-centre mixture
+    queries per head, as a built memory's are) and every layer's query is an
+    entry plus noise.  Reports per-layer time of both lookups and the
+    two-level lookup's recall@1 against the flat search."""
+    import torch
+    from attention_state_memory_amd import api, synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def to_dev(x):
+        x = np.ascontiguousarray(x)
+        if x.dtype == np.uint16:
+            return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(x).to(dev)
+
+    K, Hq = 8192, 32
+    L = []
+    for l in range(layers):
+        inp = synth.decode_inputs([6, l], B=1, Hq=Hq, Hkv=8, d=128, K=K, kv_lens=[2048])
+        C = synth.mixture_queries([6, l, 1], Hq, K, 128, M=64)
+        r = np.random.default_rng([6, l, 2])
+        pick = r.integers(0, K, Hq)
+        q = synth.bf16_bits_to_float(C)[np.arange(Hq), pick][None] + \
+            np.float32(0.3) * r.standard_normal((1, Hq, 128), dtype=np.float32)
+        t = {k: to_dev(inp[k]) for k in ("Abar", "LSEbar", "Kl", "Vl", "kv_start", "kv_len")}
+        t["q"] = to_dev(synth.to_bf16_bits(q))
+        t["C"] = to_dev(C)
+        t["cinv"] = api.centroid_inv_norms(t["C"])
+        t["index"] = api.build_index(t["C"], S, 4)
+        L.append(t)
+    torch.cuda.synchronize()
+    print("layers and indices resident", file=sys.stderr, flush=True)
+    scale = synth.softmax_scale(128)
+    out = torch.empty((layers, 1, Hq, 128), dtype=torch.float32, device=dev)
+    lse = torch.empty((layers, 1, Hq), dtype=torch.float32, device=dev)
+    idx_f = torch.empty((layers, 1, Hq), dtype=torch.int32, device=dev)
+    idx_h = torch.empty((layers, 1, Hq), dtype=torch.int32, device=dev)
+    ws = torch.zeros(max(api.decode_step_ws(api.BF16, 1, Hq, 8, 128, K, 2048),
+                         int(api.lib().asm_decode_step_hier_ws(api.BF16, 1, Hq, 8, 128, K, S, p, 2048))),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.Stream(dev)
+
+    def flat(l):
+        t = L[l]
+        api.decode_step(t["q"], t["C"], t["cinv"], t["Abar"], t["LSEbar"], t["Kl"], t["Vl"],
+                        t["kv_start"], t["kv_len"], 2048, scale, out=out[l], out_lse=lse[l],
+                        out_idx=idx_f[l], workspace=ws)
+
+    def hier(l):
+        t = L[l]
+        api.decode_step_hier(t["q"], t["C"], t["cinv"], t["index"], p, t["Abar"], t["LSEbar"],
+                             t["Kl"], t["Vl"], t["kv_start"], t["kv_len"], 2048, scale,
+                             out=out[l], out_lse=lse[l], out_idx=idx_h[l], workspace=ws)
+
+    def timed(fn):
+        with torch.cuda.stream(stream):
+            for l in range(layers):
+                fn(l)
+        stream.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for l in range(layers):
+                fn(l)
+        with torch.cuda.stream(stream):
+            g.replay()
+        stream.synchronize()
+        reps = max(1, args.steps // 8)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            for _ in range(reps):
+                g.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps, reps
+
+    ms_flat, _ = timed(flat)
+    ms_hier, reps = timed(hier)
+    recall = float((idx_f == idx_h).float().mean().item())
+    rows = p * K / S  # member rows scanned per query head on average
+    hier_bytes = layers * (Hq * (S * 128 * 2 + S * 4 + (S + 1) * 4 + rows * (128 * 2 + 4 + 4) + 128 * 2
+                                 + (128 * 4 + 4) + (128 * 4 + 8)) + 8 * 2048 * 128 * 2 * 2 + 8)
+    gbs = hier_bytes / (ms_hier * 1e-3) / 1e9
+    result = {
+        "metric": "ASM decode, batch 1 through 32 layers at K=8192, two-level lookup: per-layer latency",
+        "value": ms_hier * 1e3 / layers, "unit": "us/layer", "n_gpus": 1, "steps": reps,
+        "warmup": args.warmup, "ms_per_step": ms_hier, "higher_is_better": False,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (64-centre mixture entries per head, queries = entries + noise, "
+                "N(0,1) bf16 local KV, fp32 states)",
+        "config": {"workload": "layer_decode_hier", "layers": layers, "K": K, "supers": S,
+                   "probes": p, "batch": 1, "q_heads": Hq, "kv_heads": 8, "head_dim": 128,
+                   "local_len": 2048, "launch": "hip_graph"},
+        "flat_us_per_layer": ms_flat * 1e3 / layers,
+        "speedup_vs_flat": ms_flat / ms_hier,
+        "recall_at_1_vs_flat": recall,
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                     "algorithmic_bytes_per_step": hier_bytes,
+                     "timed": "HIP events around replays of one graph holding the 32 layers' "
+                              "asm_decode_step_hier calls"},
     }
     print(json.dumps(result), flush=True)
 

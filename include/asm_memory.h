@@ -134,11 +134,12 @@ int asm_decode_step(int dtype, int B, int Hq, int Hkv, int d, int K, float scale
  *   SC [Hq, S, d] bf16; scinv [Hq, S]; offsets [Hq, S+1]; members [Hq, K]
  *   int32: as written by asm_build_index.
  *   out_probes [B, Hq, p] int32 (nullable): the probed supers, best first,
- *   -1 past the number of non-empty supers.
+ *   -1 past the number of non-empty supers.  The probes of rank p-1 and
+ *   below that tie exactly in score resolve to the lower super index.
  *   Other arguments as asm_decode_step; the workspace size comes from
  *   asm_decode_step_hier_ws.
  */
-size_t asm_decode_step_hier_ws(int dtype, int B, int Hq, int Hkv, int d, int K, int S,
+size_t asm_decode_step_hier_ws(int dtype, int B, int Hq, int Hkv, int d, int K, int S, int p,
                                int max_kv_len);
 int asm_decode_step_hier(int dtype, int B, int Hq, int Hkv, int d, int K, int S, int p,
                          float scale, const void* q, const void* C, const float* cinv,
