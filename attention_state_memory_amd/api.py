@@ -42,6 +42,9 @@ SIGNATURES = {
     "asm_aggregate_ws": (_c_size, [_c_int] * 5),
     "asm_aggregate": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int,
                                _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_size, _vp]),
+    "asm_build_states_streamed_ws": (_c_size, [_c_int] * 6),
+    "asm_build_states_streamed": (_c_int, [_c_int] * 7 + [_c_float, _vp, _vp, _vp, _vp, _vp,
+                                                          _c_int, _vp, _c_size, _vp, _vp]),
     "asm_build_index_ws": (_c_size, [_c_int] * 5),
     "asm_build_index": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                  _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_size, _vp]),
@@ -215,6 +218,39 @@ def build_states(Q, Kp, Vp, chunk: int, scale: float, *, A=None, LSE=None,
         _ptr(Ac), _ptr(Lc), _ptr(A), _ptr(LSE), int(bool(accumulate)), _ptr(ws), nbytes,
         _stream(dev)))
     return A, LSE, Ac, Lc
+
+
+def build_states_streamed(Q, Kp_host, Vp_host, chunk: int, scale: float, *, A=None, LSE=None,
+                          accumulate: bool = False, workspace=None, copy_stream=None):
+    """Prefix states for a prefix in host memory.  Q [Hq, N, d] on the GPU;
+    Kp_host, Vp_host [Hkv, L, d] CPU tensors (pinned for overlap).  The
+    copies run on `copy_stream` (a new default-priority stream if None)
+    while the current stream encodes.  Returns (A [Hq, N, d], LSE [Hq, N])."""
+    _dev(Q, "Q")
+    for t, name in ((Kp_host, "Kp_host"), (Vp_host, "Vp_host")):
+        if not isinstance(t, torch.Tensor) or t.is_cuda or not t.is_contiguous():
+            raise TypeError(f"{name} must be a contiguous CPU tensor")
+        if t.dtype != Q.dtype:
+            raise TypeError("Q, Kp_host and Vp_host must share one dtype")
+    code = _dtype_code(Q)
+    Hq, N, d = Q.shape
+    Hkv, L, _ = Kp_host.shape
+    dev = Q.device
+    if A is None:
+        A = torch.empty((Hq, N, d), dtype=torch.float32, device=dev)
+    if LSE is None:
+        LSE = torch.empty((Hq, N), dtype=torch.float32, device=dev)
+    _dev(A, "A", torch.float32)
+    _dev(LSE, "LSE", torch.float32)
+    if copy_stream is None:
+        copy_stream = torch.cuda.Stream(device=dev)
+    nbytes = int(lib().asm_build_states_streamed_ws(code, Hq, Hkv, N, d, int(chunk)))
+    ws = _workspace(nbytes, dev, workspace)
+    _check("asm_build_states_streamed", lib().asm_build_states_streamed(
+        code, Hq, Hkv, N, L, d, int(chunk), float(scale), _ptr(Q), Kp_host.data_ptr(),
+        Vp_host.data_ptr(), _ptr(A), _ptr(LSE), int(bool(accumulate)), _ptr(ws), nbytes,
+        _stream(dev), ctypes.c_void_p(copy_stream.cuda_stream)))
+    return A, LSE
 
 
 def kmeans_assign(X, C, cinv, *, idx=None, best=None, want_best: bool = False, workspace=None):

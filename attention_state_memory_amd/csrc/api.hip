@@ -372,6 +372,99 @@ int asm_build_states(int dtype, int Hq, int Hkv, int N, int L, int d, int chunk,
   return hip_status(asmk::launch_build_states(a, dtype, stream), "build_states");
 }
 
+// Streamed prefix: chunk c is staged into slot c % 2 of the workspace on the
+// copy stream while the compute stream encodes chunk c - 1; each chunk is
+// one asm_build_states call that merges into (A, LSE).
+namespace {
+size_t stream_slot_bytes(int dtype, int Hkv, int d, int chunk) {
+  const size_t esz = dtype == ASM_BF16 ? 2 : 4;
+  return asmk::align_up(size_t(Hkv) * chunk * d * esz, kAlign);
+}
+
+struct EventSet {
+  hipEvent_t e[5] = {nullptr, nullptr, nullptr, nullptr, nullptr};
+  ~EventSet() {
+    for (hipEvent_t x : e)
+      if (x) (void)hipEventDestroy(x);
+  }
+};
+}  // namespace
+
+size_t asm_build_states_streamed_ws(int dtype, int Hq, int Hkv, int N, int d, int chunk) {
+  if (check_dtype(dtype) != ASM_OK || check_d(dtype, d) != ASM_OK || Hq < 1 || Hkv < 1 ||
+      Hq % Hkv != 0 || N < 0 || chunk < 1)
+    return 0;
+  return 4 * stream_slot_bytes(dtype, Hkv, d, chunk) +
+         asmk::align_up(asmk::states_ws_bytes(dtype, Hq, Hkv, N, chunk, d), kAlign);
+}
+
+int asm_build_states_streamed(int dtype, int Hq, int Hkv, int N, int L, int d, int chunk,
+                              float scale, const void* Q, const void* Kp_host,
+                              const void* Vp_host, float* A, float* LSE, int accumulate,
+                              void* ws, size_t ws_bytes, hipStream_t stream,
+                              hipStream_t copy_stream) {
+  ASM_TRY(check_dtype(dtype));
+  ASM_TRY(check_d(dtype, d));
+  if (Hq < 1 || Hkv < 1 || N < 0 || L < 0 || chunk < 1)
+    return fail(ASM_ERR_SHAPE, "need Hq, Hkv, chunk >= 1 and N, L >= 0");
+  if (Hq % Hkv != 0) return fail(ASM_ERR_SHAPE, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  if (N == 0) return ok();
+  if (!Q || !A || !LSE) return fail(ASM_ERR_NULL, "Q, A and LSE are required");
+  if (L > 0 && (!Kp_host || !Vp_host)) return fail(ASM_ERR_NULL, "Kp and Vp are required when L > 0");
+  const size_t need = asm_build_states_streamed_ws(dtype, Hq, Hkv, N, d, chunk);
+  if (need == 0) return fail(ASM_ERR_SHAPE, "unsupported shape");
+  ASM_TRY(check_ws(ws, ws_bytes, need));
+  if (L == 0) {
+    // no prefix: the states of an empty prefix, through the plain entry point
+    return asm_build_states(dtype, Hq, Hkv, N, 0, d, chunk, scale, Q, nullptr, nullptr, nullptr,
+                            nullptr, A, LSE, accumulate, nullptr, 0, stream);
+  }
+  const size_t esz = dtype == ASM_BF16 ? 2 : 4;
+  const size_t slot = stream_slot_bytes(dtype, Hkv, d, chunk);
+  char* w = static_cast<char*>(ws);
+  void* states_ws = w + 4 * slot;
+  const size_t states_ws_bytes = ws_bytes - 4 * slot;
+  // one stream given (or the same twice): copies and compute share it
+  const bool two = copy_stream != stream;
+  hipStream_t cs = two ? copy_stream : stream;
+  EventSet ev;  // [0] start, [1..2] slot ready, [3..4] slot free
+  for (hipEvent_t& e : ev.e) {
+    const int st = hip_status(hipEventCreateWithFlags(&e, hipEventDisableTiming), "event create");
+    if (st != ASM_OK) return st;
+  }
+  if (two) {
+    // staging may still be read by earlier work on the compute stream
+    ASM_TRY(hip_status(hipEventRecord(ev.e[0], stream), "event record"));
+    ASM_TRY(hip_status(hipStreamWaitEvent(cs, ev.e[0], 0), "stream wait"));
+  }
+  const int nc = int((int64_t(L) + chunk - 1) / chunk);
+  for (int c = 0; c < nc; ++c) {
+    const int sl = c & 1;
+    const int64_t t0 = int64_t(c) * chunk;
+    const int len = int(L - t0 < chunk ? L - t0 : chunk);
+    char* kd = w + (2 * sl) * slot;
+    char* vd = w + (2 * sl + 1) * slot;
+    if (two && c >= 2) ASM_TRY(hip_status(hipStreamWaitEvent(cs, ev.e[3 + sl], 0), "stream wait"));
+    // [Hkv, L, d] host rows t0 .. t0+len of every kv head -> [Hkv, len, d]
+    const size_t row = size_t(len) * d * esz, spitch = size_t(L) * d * esz;
+    ASM_TRY(hip_status(hipMemcpy2DAsync(kd, row, static_cast<const char*>(Kp_host) + t0 * d * esz,
+                                        spitch, row, size_t(Hkv), hipMemcpyHostToDevice, cs),
+                       "copy K"));
+    ASM_TRY(hip_status(hipMemcpy2DAsync(vd, row, static_cast<const char*>(Vp_host) + t0 * d * esz,
+                                        spitch, row, size_t(Hkv), hipMemcpyHostToDevice, cs),
+                       "copy V"));
+    if (two) {
+      ASM_TRY(hip_status(hipEventRecord(ev.e[1 + sl], cs), "event record"));
+      ASM_TRY(hip_status(hipStreamWaitEvent(stream, ev.e[1 + sl], 0), "stream wait"));
+    }
+    ASM_TRY(asm_build_states(dtype, Hq, Hkv, N, len, d, len, scale, Q, kd, vd, nullptr, nullptr,
+                             A, LSE, (c > 0 || accumulate) ? 1 : 0, states_ws, states_ws_bytes,
+                             stream));
+    if (two) ASM_TRY(hip_status(hipEventRecord(ev.e[3 + sl], stream), "event record"));
+  }
+  return ok();
+}
+
 // ---------------------------------------------------------------------------
 size_t asm_kmeans_assign_ws(int dtype, int H, int N, int K, int d) {
   (void)dtype; (void)H; (void)N; (void)K; (void)d;

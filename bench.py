@@ -103,7 +103,7 @@ def parse():
                         "timed region, as the reference kernel for HBM byte counters")
     p.add_argument("--workload", default="batched_decode",
                    choices=("batched_decode", "layer_decode", "layer_decode_hier", "prefix_states",
-                            "memory_build"),
+                            "prefix_states_streamed", "memory_build"),
                    help="batched_decode (the headline metric) or one of the offline build "
                         "workloads, reported on their MFMA rooflines")
     return p.parse_args()
@@ -567,6 +567,10 @@ def run_build(args):
         print(json.dumps(result), flush=True)
         return
 
+    if args.workload == "prefix_states_streamed":
+        run_streamed(args, w=synth.prefix_states(), to_dev=to_dev)
+        return
+
     # memory_build: states over the prefix, 10 Lloyd iterations, aggregation
     w = synth.memory_build()
     print("memory_build inputs generated", file=sys.stderr, flush=True)
@@ -640,6 +644,75 @@ def run_build(args):
     }
     if args.cpu_seconds > 0:
         result["cpu_baseline"] = cpu_baseline_assign(w, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def run_streamed(args, w, to_dev):
+    """The prefix-state workload with the prefix in pinned host memory:
+    asm_build_states_streamed copies chunk c + 1 while chunk c is encoded.
+    Timed beside it, on the same stream: the resident asm_build_states over
+    the same chunks (merged states only) and the plain host-to-device copy
+    of the prefix."""
+    import torch
+    from attention_state_memory_amd import api
+
+    dev = torch.device("cuda:0")
+    Hq, Hkv, N, L, d, chunk = w["Hq"], w["Hkv"], w["N"], w["L"], w["d"], w["chunk"]
+
+    def pinned(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).pin_memory()
+
+    Q = to_dev(w["Q"])
+    Kh, Vh = pinned(w["Kp"]), pinned(w["Vp"])
+    Kd, Vd = Kh.to(dev), Vh.to(dev)
+    A = torch.empty((Hq, N, d), dtype=torch.float32, device=dev)
+    LSE = torch.empty((Hq, N), dtype=torch.float32, device=dev)
+    ws_s = torch.zeros(int(api.lib().asm_build_states_streamed_ws(api.BF16, Hq, Hkv, N, d, chunk)),
+                       dtype=torch.uint8, device=dev)
+    ws_r = torch.zeros(max(1, int(api.lib().asm_build_states_ws(api.BF16, Hq, Hkv, N, L, d, chunk))),
+                       dtype=torch.uint8, device=dev)
+    copy_stream = torch.cuda.Stream(device=dev)
+    Kc, Vc = torch.empty_like(Kd), torch.empty_like(Vd)
+
+    def streamed():
+        api.build_states_streamed(Q, Kh, Vh, chunk, w["scale"], A=A, LSE=LSE, workspace=ws_s,
+                                  copy_stream=copy_stream)
+
+    def resident():
+        api.build_states(Q, Kd, Vd, chunk, w["scale"], A=A, LSE=LSE, workspace=ws_r)
+
+    def copy_only():
+        Kc.copy_(Kh, non_blocking=True)
+        Vc.copy_(Vh, non_blocking=True)
+
+    for fn in (streamed, resident, copy_only):
+        for _ in range(args.warmup):
+            fn()
+    steps = args.steps
+    ms = _timed(streamed, steps)
+    ms_res = _timed(resident, steps)
+    ms_copy = _timed(copy_only, steps)
+    prefix_bytes = 2 * Hkv * L * d * 2
+    flops = 4.0 * Hq * N * L * d
+    tflops = flops / (ms * 1e-3) / 1e12
+    result = {
+        "metric": "prefix attention states (query-heads x prefix tokens) per second, prefix "
+                  "streamed from pinned host memory",
+        "value": Hq * N / (ms * 1e-3), "unit": "query-head states/s", "n_gpus": 1,
+        "steps": steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded 64-centre mixture queries, N(0,1) bf16 prefix in pinned host memory)",
+        "config": {"workload": "prefix_states_streamed", "q_heads": Hq, "kv_heads": Hkv,
+                   "head_dim": d, "queries_per_head": N, "prefix": L, "chunk": chunk},
+        "resident_ms": ms_res,
+        "copy_only_ms": ms_copy,
+        "host_to_device_GBps": prefix_bytes / (ms * 1e-3) / 1e9,
+        "copy_only_GBps": prefix_bytes / (ms_copy * 1e-3) / 1e9,
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": BF16_MFMA_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": tflops / BF16_MFMA_PEAK_TFLOPS, "traffic": None,
+                     "algorithmic_flops_per_launch": flops,
+                     "timed": "asm_build_states_streamed (copies and one states launch per chunk)"},
+    }
     print(json.dumps(result), flush=True)
 
 

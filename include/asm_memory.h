@@ -60,7 +60,7 @@ enum asm_status_code {
 enum asm_dtype { ASM_BF16 = 0, ASM_F32 = 1 };
 
 /* ABI version of this header (bumped on any signature change). */
-#define ASM_ABI_VERSION 2
+#define ASM_ABI_VERSION 3
 int asm_abi_version(void);
 
 /* Static text for a status code. */
@@ -178,6 +178,38 @@ int asm_build_states(int dtype, int Hq, int Hkv, int N, int L, int d, int chunk,
                      const void* Q, const void* Kp, const void* Vp,
                      float* A_chunks, float* LSE_chunks, float* A, float* LSE, int accumulate,
                      void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * asm_build_states_streamed -- asm_build_states (A_chunks = LSE_chunks =
+ * NULL) for a prefix held in host memory ([TS] Eficiencia: chunks are
+ * encoded independently and merged, so the prefix need not be resident).
+ * Chunk c (prefix tokens [c*chunk, min(L, (c+1)*chunk)) of every kv head) is
+ * copied into one of two device staging slots on copy_stream while `stream`
+ * encodes the previous chunk; each chunk then runs as one asm_build_states
+ * call that merges into (A, LSE) (the first one with the caller's
+ * `accumulate`).  The results equal asm_build_states on the same prefix
+ * with the same chunk bit for bit: the chunk-end merge is the same
+ * arithmetic.
+ *   Kp_host, Vp_host [Hkv, L, d] dtype in host memory.  Pinned memory
+ *   (hipHostMalloc) lets the copies overlap the compute; pageable memory
+ *   works, with copies that do not overlap.  The host buffers must stay
+ *   valid and unchanged until `stream` has passed this call's work.
+ *   Q, A, LSE, scale, accumulate: as asm_build_states (device memory).
+ *   ws: asm_build_states_streamed_ws bytes of device memory (four staging
+ *   slots of Hkv*chunk*d elements, then asm_build_states' workspace).
+ *   copy_stream: a stream distinct from `stream` for the copies; passing
+ *   `stream` itself (or the same NULL stream) serialises copies and compute.
+ *   On return all work is enqueued; `stream` is ordered after every copy and
+ *   encode, copy_stream after the copies only.  Returns ASM_ERR_HIP if an
+ *   event, copy or launch fails (work enqueued before the failure stays
+ *   enqueued).
+ */
+size_t asm_build_states_streamed_ws(int dtype, int Hq, int Hkv, int N, int d, int chunk);
+int asm_build_states_streamed(int dtype, int Hq, int Hkv, int N, int L, int d, int chunk,
+                              float scale, const void* Q, const void* Kp_host,
+                              const void* Vp_host, float* A, float* LSE, int accumulate,
+                              void* ws, size_t ws_bytes, hipStream_t stream,
+                              hipStream_t copy_stream);
 
 /*
  * asm_kmeans_assign -- nearest centroid by cosine for every collected query
