@@ -40,6 +40,11 @@ notes with its reason):
   members' a_i ([TS] Agregación: merge with the online-softmax rule into a
   lossless average).
 
+* Whitening at retrieval ([TS] Recuperación, optional): x -> W (x - mu) fit
+  per head on the calibration queries, W the symmetric inverse square root of
+  their ridged population covariance; whitened rows are rounded once to the
+  table's type and scored by cosine.
+
 Inputs arrive as float64 arrays.  bf16 data arrive as uint16 bit patterns and
 are widened with `bf16_bits_to_f64` (exact); float32 data with `f32_to_f64`
 (exact).
@@ -472,3 +477,54 @@ def lookup_hier(q, C, SC, e2s, counts, p: int):
     probes, _ = probe_supers(q, SC, counts, p)
     idx, _, _ = lookup_probed(q, C, e2s, probes)
     return idx, probes
+
+
+# --------------------------------------------------------------------------
+# Whitening at retrieval
+# [TS] Recuperación: the nearest centroid is found by cosine similarity,
+# optionally after a whitening transform.  The pages say no more; the reading
+# taken: the transform is fit per head on that head's calibration queries X
+# (the Recolección corpus) as the standard whitening x -> W (x - mu), with mu
+# the mean of X, Sigma the population covariance of X plus a small ridge
+# eps * I (eps = ridge * trace(Sigma) / d, ridge = 1e-6 by default, so that a
+# rank-deficient corpus still has a whitening), and W = Sigma^(-1/2), the
+# symmetric inverse square root.  Both the query and the table rows are
+# mapped and rounded once to the table's type, then scored by cosine exactly
+# as in the plain lookup; the merge uses the raw query.
+# --------------------------------------------------------------------------
+
+
+def whiten_fit(X, ridge: float = 1e-6):
+    """(mu [d], W [d, d]) of the calibration queries X [N, d]: mean, ridged
+    population covariance, and its symmetric inverse square root from the
+    eigendecomposition Sigma = V diag(lam) V^T, W = V diag(lam^-1/2) V^T."""
+    X = np.asarray(X, dtype=np.float64)
+    N, d = X.shape
+    mu = X.mean(axis=0)
+    Xc = X - mu
+    Sigma = Xc.T @ Xc / N
+    Sigma = Sigma + (ridge * np.trace(Sigma) / d) * np.eye(d)
+    lam, V = np.linalg.eigh(Sigma)
+    W = (V * (1.0 / np.sqrt(lam))) @ V.T
+    return mu, W
+
+
+def whiten_apply(Y, mu, W):
+    """W (y - mu) for every row y of Y [..., d], in float64 (no rounding)."""
+    Y = np.asarray(Y, dtype=np.float64)
+    return (Y - mu) @ np.asarray(W, dtype=np.float64).T
+
+
+def whiten_rows(Y, mu, W, dtype: str):
+    """whiten_apply rounded once to the storage type, widened back to
+    float64: the whitened table or query as it is stored and scored."""
+    return round_to_dtype(whiten_apply(Y, mu, W), dtype)
+
+
+def lookup_whitened(q, C, mu, W, dtype: str):
+    """Nearest table row of each query row q [M, d] after whitening both
+    sides (rounded to dtype): (idx [M], cos [M, K]) as in `assign`."""
+    qw = whiten_rows(np.atleast_2d(q), mu, W, dtype)
+    Cw = whiten_rows(C, mu, W, dtype)
+    idx, cs, _ = assign(qw, Cw)
+    return idx, cs

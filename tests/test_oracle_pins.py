@@ -561,3 +561,88 @@ def test_index_members_against_brute_force():
         expect = [k for k in range(300) if e2s[k] == s]
         assert list(members[offsets[s]:offsets[s + 1]]) == expect
     assert offsets[-1] == 300
+
+
+# ---------------------------------------------------------------- whitening
+
+def test_whiten_hand_worked_2d(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "whiten_2d_hand.json")))
+    for case in g["cases"]:
+        X = np.array(case["X"], float)
+        mu, W = O.whiten_fit(X, ridge=0.0)
+        np.testing.assert_allclose(mu, case["mu"], rtol=0, atol=1e-15)
+        np.testing.assert_allclose(W, case["W"], rtol=0, atol=1e-14)
+        np.testing.assert_allclose(O.whiten_apply(X, mu, W), case["whitened"], rtol=0, atol=1e-14)
+
+
+def test_whiten_recovers_a_known_covariance_with_its_ridge():
+    """Rows mu0 + A z over the 16 sign patterns z in {-1, 1}^4 have mean mu0
+    and population covariance A A^T exactly.  With A = H diag(s), H the
+    orthonormal 4x4 Hadamard matrix, W must be H diag((s^2 + eps)^-1/2) H^T
+    with eps = 1e-6 * trace / 4."""
+    Z = np.array([[1 - 2 * ((i >> b) & 1) for b in range(4)] for i in range(16)], float)
+    Hd = 0.5 * np.array([[1, 1, 1, 1], [1, -1, 1, -1], [1, 1, -1, -1], [1, -1, -1, 1]], float)
+    s = np.array([1.0, 2.0, 3.0, 0.5])
+    mu0 = np.array([0.25, -1.0, 4.0, 2.5])
+    X = mu0 + Z @ (Hd * s).T
+    mu, W = O.whiten_fit(X)
+    eps = 1e-6 * np.sum(s ** 2) / 4
+    W_ref = (Hd * (1.0 / np.sqrt(s ** 2 + eps))) @ Hd.T
+    np.testing.assert_allclose(mu, mu0, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(W, W_ref, rtol=0, atol=1e-12)
+
+
+def test_whitened_corpus_covariance_closed_form():
+    """cov(W (x - mu)) over the corpus is I - eps (Sigma + eps I)^-1 (numpy's
+    cov and inv), and exactly I without ridge; the mean is 0."""
+    r = rng(40, 1)
+    X = r.standard_normal((500, 6)) @ r.standard_normal((6, 6)) + r.standard_normal(6)
+    for ridge in (0.0, 1e-6, 1e-2):
+        mu, W = O.whiten_fit(X, ridge=ridge)
+        Y = O.whiten_apply(X, mu, W)
+        S0 = np.cov(X.T, bias=True)
+        eps = ridge * np.trace(S0) / 6
+        ref = np.eye(6) - eps * np.linalg.inv(S0 + eps * np.eye(6))
+        np.testing.assert_allclose(np.cov(Y.T, bias=True), ref, rtol=0, atol=1e-10)
+        np.testing.assert_allclose(Y.mean(axis=0), 0.0, rtol=0, atol=1e-12)
+
+
+def test_whitened_distance_is_mahalanobis():
+    """|W (u - v)| is scipy's Mahalanobis distance under the ridged
+    covariance: W^T W is the inverse covariance."""
+    r = rng(40, 2)
+    X = r.standard_normal((300, 5)) * np.array([1.0, 3.0, 0.2, 1.0, 2.0])
+    mu, W = O.whiten_fit(X)
+    S0 = np.cov(X.T, bias=True)
+    VI = np.linalg.inv(S0 + 1e-6 * np.trace(S0) / 5 * np.eye(5))
+    for _ in range(5):
+        u, v = r.standard_normal(5), r.standard_normal(5)
+        ref = scipy.spatial.distance.mahalanobis(u, v, VI)
+        assert abs(np.linalg.norm(O.whiten_apply(u, mu, W) - O.whiten_apply(v, mu, W)) - ref) < 1e-12
+
+
+def test_whitened_cosine_is_affine_invariant():
+    """Without ridge, refitting on an affinely transformed corpus (x M + b)
+    leaves every whitened cosine unchanged."""
+    r = rng(40, 3)
+    X = r.standard_normal((400, 4)) @ r.standard_normal((4, 4))
+    M = r.standard_normal((4, 4)) + 2 * np.eye(4)
+    b = r.standard_normal(4)
+    q, C = r.standard_normal((3, 4)), r.standard_normal((7, 4))
+    mu, W = O.whiten_fit(X, ridge=0.0)
+    mu2, W2 = O.whiten_fit(X @ M + b, ridge=0.0)
+    c1 = O.cosine(O.whiten_apply(q, mu, W), O.whiten_apply(C, mu, W))
+    c2 = O.cosine(O.whiten_apply(q @ M + b, mu2, W2), O.whiten_apply(C @ M + b, mu2, W2))
+    np.testing.assert_allclose(c1, c2, rtol=0, atol=1e-10)
+
+
+def test_lookup_whitened_identity_transform_is_plain_lookup():
+    """mu = 0 and W = I leave bf16 rows unchanged, so the whitened lookup is
+    the plain cosine lookup."""
+    r = rng(40, 4)
+    C = O.round_to_dtype(r.standard_normal((50, 8)), "bf16")
+    q = O.round_to_dtype(r.standard_normal((20, 8)), "bf16")
+    idx, cs = O.lookup_whitened(q, C, np.zeros(8), np.eye(8), "bf16")
+    idx0, cs0, _ = O.assign(q, C)
+    np.testing.assert_array_equal(idx, idx0)
+    np.testing.assert_array_equal(cs, cs0)
