@@ -33,6 +33,16 @@ SIGNATURES = {
                                  _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                  _c_i64, _c_i64, _c_i64, _vp, _vp, _c_int,
                                  _vp, _vp, _vp, _vp, _c_size, _vp]),
+    "asm_whiten_fit_ws": (_c_size, [_c_int] * 4),
+    "asm_whiten_fit": (_c_int, [_c_int] * 4 + [_vp, ctypes.c_double, _vp, _vp, _vp, _vp, _c_size,
+                                               _vp]),
+    "asm_whiten_rows": (_c_int, [_c_int, _c_int, _c_i64, _c_int, _vp, _c_i64, _c_i64, _vp, _vp,
+                                 _vp, _vp]),
+    "asm_decode_step_whitened_ws": (_c_size, [_c_int] * 7),
+    "asm_decode_step_whitened": (_c_int, [_c_int] * 6 + [_c_float, _vp, _vp, _vp, _vp, _vp, _vp,
+                                                          _vp, _vp, _vp, _c_i64, _c_i64, _c_i64,
+                                                          _vp, _vp, _c_int, _vp, _vp, _vp, _vp,
+                                                          _c_size, _vp]),
     "asm_build_states_ws": (_c_size, [_c_int] * 7),
     "asm_build_states": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_float,
                                   _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_int, _vp, _c_size, _vp]),
@@ -181,6 +191,81 @@ def decode_step(q, C, cinv, Abar, LSEbar, Kl, Vl, kv_start, kv_len, max_kv_len: 
     _check("asm_decode_step", lib().asm_decode_step(
         code, B, Hq, Hkv, d, K, float(scale), _ptr(q), _ptr(C), _ptr(cinv), _ptr(Abar),
         _ptr(LSEbar), _ptr(Kl), _ptr(Vl), Kl.stride(0), Kl.stride(1), cap,
+        _ptr(kv_start), _ptr(kv_len), int(max_kv_len), _ptr(out), _ptr(out_lse), _ptr(out_idx),
+        _ptr(ws), nbytes, _stream(dev)))
+    return out, out_lse, out_idx
+
+
+def whiten_fit(X, ridge: float = 1e-6, *, want_resid: bool = False, workspace=None):
+    """Whitening transforms of the calibration queries X [H, N, d]: returns
+    (mu [H, d] f64, W [H, d, d] f64, resid [H] f64 | None)."""
+    _dev(X, "X")
+    code = _dtype_code(X)
+    H, N, d = X.shape
+    dev = X.device
+    mu = torch.empty((H, d), dtype=torch.float64, device=dev)
+    W = torch.empty((H, d, d), dtype=torch.float64, device=dev)
+    resid = torch.empty((H,), dtype=torch.float64, device=dev) if want_resid else None
+    nbytes = int(lib().asm_whiten_fit_ws(code, H, N, d))
+    ws = _workspace(nbytes, dev, workspace)
+    _check("asm_whiten_fit", lib().asm_whiten_fit(
+        code, H, N, d, _ptr(X), float(ridge), _ptr(mu), _ptr(W), _ptr(resid), _ptr(ws), nbytes,
+        _stream(dev)))
+    return mu, W, resid
+
+
+def whiten_rows(Y, mu, W, *, out=None):
+    """Whitened rows of a head-major table Y [H, M, d]: round(W[h] (y - mu[h]))."""
+    _dev(Y, "Y")
+    _dev(mu, "mu", torch.float64)
+    _dev(W, "W", torch.float64)
+    H, M, d = Y.shape
+    if out is None:
+        out = torch.empty_like(Y)
+    _dev(out, "out", Y.dtype)
+    _check("asm_whiten_rows", lib().asm_whiten_rows(
+        _dtype_code(Y), H, M, d, _ptr(Y), M * d, d, _ptr(mu), _ptr(W), _ptr(out),
+        _stream(Y.device)))
+    return out
+
+
+def decode_step_whitened(q, mu, W, Cw, cwinv, Abar, LSEbar, Kl, Vl, kv_start, kv_len,
+                         max_kv_len: int, scale: float, *, out=None, out_lse=None, out_idx=None,
+                         workspace=None):
+    """decode_step with the lookup on whitened queries against the whitened
+    table Cw (cwinv its inverse norms).  Returns (out, out_lse, idx)."""
+    for t, n in ((q, "q"), (Cw, "Cw")):
+        _dev(t, n)
+    _dev(mu, "mu", torch.float64)
+    _dev(W, "W", torch.float64)
+    _dev(cwinv, "cwinv", torch.float32)
+    _dev(Abar, "Abar", torch.float32)
+    _dev(LSEbar, "LSEbar", torch.float32)
+    _dev(kv_start, "kv_start", torch.int32)
+    _dev(kv_len, "kv_len", torch.int32)
+    code = _dtype_code(q)
+    if Cw.dtype != q.dtype or Kl.dtype != q.dtype or Vl.dtype != q.dtype:
+        raise TypeError("q, Cw, Kl and Vl must share one dtype")
+    for t, n in ((Kl, "Kl"), (Vl, "Vl")):
+        if not t.is_cuda or t.dim() != 3 or t.stride(2) != 1:
+            raise ValueError(f"{n} must be a [Hkv, capacity, d] CUDA tensor with d contiguous")
+    if Kl.stride() != Vl.stride() or Kl.shape != Vl.shape:
+        raise ValueError("Kl and Vl must share shape and strides")
+    B, Hq, d = q.shape
+    K = Cw.shape[1]
+    Hkv, cap, _ = Kl.shape
+    dev = q.device
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+    if out_lse is None:
+        out_lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    if out_idx is None:
+        out_idx = torch.empty((B, Hq), dtype=torch.int32, device=dev)
+    nbytes = int(lib().asm_decode_step_whitened_ws(code, B, Hq, Hkv, d, K, int(max_kv_len)))
+    ws = _workspace(nbytes, dev, workspace)
+    _check("asm_decode_step_whitened", lib().asm_decode_step_whitened(
+        code, B, Hq, Hkv, d, K, float(scale), _ptr(q), _ptr(mu), _ptr(W), _ptr(Cw), _ptr(cwinv),
+        _ptr(Abar), _ptr(LSEbar), _ptr(Kl), _ptr(Vl), Kl.stride(0), Kl.stride(1), cap,
         _ptr(kv_start), _ptr(kv_len), int(max_kv_len), _ptr(out), _ptr(out_lse), _ptr(out_idx),
         _ptr(ws), nbytes, _stream(dev)))
     return out, out_lse, out_idx

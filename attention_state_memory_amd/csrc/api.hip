@@ -171,15 +171,17 @@ int validate_decode_shape(int dtype, int B, int Hq, int Hkv, int d, int K, int m
   return ASM_OK;
 }
 
-// The decode step for both lookups; `hier` (hierarchical lookup) is NULL for
-// the flat search.
+// The decode step for every lookup; `hier` (hierarchical lookup) is NULL for
+// the flat search; `qs` (the queries the lookup scores) is NULL when they are
+// the queries themselves.
 int decode_impl(int dtype, int B, int Hq, int Hkv, int d, int K, float scale,
                 const void* q, const void* C, const float* cinv, const float* Abar,
                 const float* LSEbar, const void* Kl, const void* Vl,
                 int64_t kv_head_stride, int64_t kv_tok_stride, int64_t kv_capacity,
                 const int32_t* kv_start, const int32_t* kv_len, int max_kv_len,
                 float* out, float* out_lse, int32_t* out_idx,
-                void* ws, size_t ws_bytes, hipStream_t stream, asmk::HierArgs* hier) {
+                void* ws, size_t ws_bytes, hipStream_t stream, asmk::HierArgs* hier,
+                const void* qs = nullptr) {
   ASM_TRY(validate_decode_shape(dtype, B, Hq, Hkv, d, K, max_kv_len));
   if (!(scale == scale) || scale == INFINITY || scale == -INFINITY)
     return fail(ASM_ERR_SHAPE, "scale must be finite");
@@ -223,6 +225,7 @@ int decode_impl(int dtype, int B, int Hq, int Hkv, int d, int K, float scale,
     const int nb = B - b0 < p.Bc ? B - b0 : p.Bc;
     a.B = nb;
     a.q = static_cast<const char*>(q) + size_t(b0) * Hq * d * esz;
+    a.qs = qs ? static_cast<const char*>(qs) + size_t(b0) * Hq * d * esz : a.q;
     a.kv_start = kv_start + b0;
     a.kv_len = kv_len + b0;
     a.out = out + size_t(b0) * Hq * d;
@@ -296,6 +299,87 @@ int asm_decode_step(int dtype, int B, int Hq, int Hkv, int d, int K, float scale
   return decode_impl(dtype, B, Hq, Hkv, d, K, scale, q, C, cinv, Abar, LSEbar, Kl, Vl,
                      kv_head_stride, kv_tok_stride, kv_capacity, kv_start, kv_len, max_kv_len,
                      out, out_lse, out_idx, ws, ws_bytes, stream, nullptr);
+}
+
+// ---------------------------------------------------------------------------
+size_t asm_whiten_fit_ws(int dtype, int H, int N, int d) {
+  if (check_dtype(dtype) != ASM_OK || (d != 64 && d != 128) || H < 1 || N < 1) return 0;
+  return asmk::whiten_fit_ws_bytes(H, N, d);
+}
+
+int asm_whiten_fit(int dtype, int H, int N, int d, const void* X, double ridge, double* mu,
+                   double* W, double* resid, void* ws, size_t ws_bytes, hipStream_t stream) {
+  ASM_TRY(check_dtype(dtype));
+  if (d != 64 && d != 128) return fail(ASM_ERR_SHAPE, "whitening needs d in {64, 128} (d=%d)", d);
+  if (H < 1 || N < 1) return fail(ASM_ERR_SHAPE, "need H, N >= 1 (H=%d, N=%d)", H, N);
+  if (int64_t(H) * N > (int64_t(1) << 31) / d) return fail(ASM_ERR_SHAPE, "H*N*d too large");
+  if (!(ridge >= 0.0) || ridge == INFINITY) return fail(ASM_ERR_SHAPE, "ridge must be finite and >= 0");
+  if (!X || !mu || !W) return fail(ASM_ERR_NULL, "X, mu and W are required");
+  ASM_TRY(check_bf16_ptrs(dtype, {X}));
+  const size_t need = asmk::whiten_fit_ws_bytes(H, N, d);
+  ASM_TRY(check_ws(ws, ws_bytes, need));
+  asmk::WhitenFitArgs a{};
+  a.H = H; a.N = N; a.d = d; a.nblk = asmk::whiten_blocks(H, N); a.max_iters = 100;
+  a.ridge = ridge; a.X = X; a.mu = mu; a.W = W; a.resid = resid;
+  char* w = static_cast<char*>(ws);
+  a.part_mean = reinterpret_cast<double*>(w);
+  w += asmk::align_up(size_t(H) * a.nblk * d * 8, kAlign);
+  a.part_cov = reinterpret_cast<double*>(w);
+  w += asmk::align_up(size_t(H) * a.nblk * d * d * 8, kAlign);
+  a.mats = reinterpret_cast<double*>(w);
+  return hip_status(asmk::launch_whiten_fit(a, dtype, stream), "whiten_fit");
+}
+
+int asm_whiten_rows(int dtype, int H, int64_t M, int d, const void* Y, int64_t head_stride,
+                    int64_t row_stride, const double* mu, const double* W, void* Yw,
+                    hipStream_t stream) {
+  ASM_TRY(check_dtype(dtype));
+  if (d != 64 && d != 128) return fail(ASM_ERR_SHAPE, "whitening needs d in {64, 128} (d=%d)", d);
+  if (H < 1 || M < 0 || head_stride < 0 || row_stride < 0)
+    return fail(ASM_ERR_SHAPE, "need H >= 1 and M, strides >= 0");
+  if (M == 0) return ok();
+  if ((M + 31) / 32 * H * (d / 16) >= (int64_t(1) << 31))
+    return fail(ASM_ERR_SHAPE, "too many rows for one launch");
+  if (!Y || !Yw || !mu || !W) return fail(ASM_ERR_NULL, "Y, Yw, mu and W are required");
+  if (Y == Yw) return fail(ASM_ERR_SHAPE, "Yw must not alias Y");
+  asmk::WhitenRowsArgs a{};
+  a.H = H; a.d = d; a.M = M; a.head_stride = head_stride; a.row_stride = row_stride;
+  a.Y = Y; a.Yw = Yw; a.mu = mu; a.W = W;
+  return hip_status(asmk::launch_whiten_rows(a, dtype, stream), "whiten_rows");
+}
+
+size_t asm_decode_step_whitened_ws(int dtype, int B, int Hq, int Hkv, int d, int K,
+                                   int max_kv_len) {
+  if (d != 64 && d != 128) return 0;
+  const size_t base = asm_decode_step_ws(dtype, B, Hq, Hkv, d, K, max_kv_len);
+  if (base == 0) return 0;
+  const size_t esz = dtype == ASM_BF16 ? 2 : 4;
+  return asmk::align_up(size_t(B) * Hq * d * esz, kAlign) + base;
+}
+
+int asm_decode_step_whitened(int dtype, int B, int Hq, int Hkv, int d, int K, float scale,
+                             const void* q, const double* mu, const double* W, const void* Cw,
+                             const float* cwinv, const float* Abar, const float* LSEbar,
+                             const void* Kl, const void* Vl, int64_t kv_head_stride,
+                             int64_t kv_tok_stride, int64_t kv_capacity, const int32_t* kv_start,
+                             const int32_t* kv_len, int max_kv_len, float* out, float* out_lse,
+                             int32_t* out_idx, void* ws, size_t ws_bytes, hipStream_t stream) {
+  ASM_TRY(check_dtype(dtype));
+  if (d != 64 && d != 128) return fail(ASM_ERR_SHAPE, "whitening needs d in {64, 128} (d=%d)", d);
+  ASM_TRY(validate_decode_shape(dtype, B, Hq, Hkv, d, K, max_kv_len));
+  if (!q || !mu || !W) return fail(ASM_ERR_NULL, "q, mu and W are required");
+  ASM_TRY(check_bf16_ptrs(dtype, {q}));
+  const size_t esz = dtype == ASM_BF16 ? 2 : 4;
+  const size_t qbytes = asmk::align_up(size_t(B) * Hq * d * esz, kAlign);
+  const size_t need = asm_decode_step_whitened_ws(dtype, B, Hq, Hkv, d, K, max_kv_len);
+  ASM_TRY(check_ws(ws, ws_bytes, need));
+  void* qw = ws;
+  // queries [B, Hq, d]: head h row b at h*d + b*Hq*d
+  ASM_TRY(asm_whiten_rows(dtype, Hq, B, d, q, d, int64_t(Hq) * d, mu, W, qw, stream));
+  return decode_impl(dtype, B, Hq, Hkv, d, K, scale, q, Cw, cwinv, Abar, LSEbar, Kl, Vl,
+                     kv_head_stride, kv_tok_stride, kv_capacity, kv_start, kv_len, max_kv_len,
+                     out, out_lse, out_idx, static_cast<char*>(ws) + qbytes, ws_bytes - qbytes,
+                     stream, nullptr, qw);
 }
 
 size_t asm_decode_step_hier_ws(int dtype, int B, int Hq, int Hkv, int d, int K, int S, int p,

@@ -79,7 +79,7 @@ __global__ void __launch_bounds__(256) score_generic(DecodeArgs a) {
   const int k = tile * 256 + t;
   const int D = a.d;
   const T* C = static_cast<const T*>(a.C) + size_t(h) * a.K * D;
-  const T* q = static_cast<const T*>(a.q);
+  const T* q = static_cast<const T*>(a.qs);
   const float ci = k < a.K ? a.cinv[size_t(h) * a.K + k] : 0.0f;
   for (int b = 0; b < a.B; ++b) {
     for (int x = t; x < D; x += 256) qs[x] = load_elem(q, (size_t(b) * a.Hq + h) * D + x);

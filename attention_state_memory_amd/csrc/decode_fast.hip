@@ -90,7 +90,7 @@ __device__ __forceinline__ void load_queries(u32x4 (&qb)[2][D / 32], const Decod
   constexpr int KS = D / 32;
   const int lane = threadIdx.x & 63;
   const int r16 = lane & 15, grp = lane >> 4;
-  const auto rq = make_rsrc(a.q, uint32_t(a.B) * a.Hq * D * 2);
+  const auto rq = make_rsrc(a.qs, uint32_t(a.B) * a.Hq * D * 2);
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
     const int b = q0 + 16 * nt + r16;

@@ -17,7 +17,8 @@ namespace asmk {
 struct DecodeArgs {
   int B, Hq, Hkv, d, K;
   float scale2;  // softmax scale * log2(e): scores are kept as base-2 logits
-  const void* q;
+  const void* q;   // [B, Hq, d] the queries the local attention uses
+  const void* qs;  // [B, Hq, d] the queries the lookup scores: q, or q whitened
   const void* C;
   const float* cinv;
   const float* Abar;
@@ -70,6 +71,32 @@ struct HierArgs {
 };
 bool hier_fast_path(int dtype, int d);
 hipError_t launch_hier_lookup(const HierArgs& a, hipStream_t s);
+
+// ---- whitening at retrieval ---------------------------------------------------
+struct WhitenFitArgs {
+  int H, N, d, nblk, max_iters;
+  double ridge;
+  const void* X;       // [H, N, d] calibration queries
+  double* part_mean;   // [H, nblk, d] workspace
+  double* part_cov;    // [H, nblk, d, d] workspace
+  double* mats;        // [H, 4, d, d] workspace (iteration matrices)
+  double* mu;          // [H, d]
+  double* W;           // [H, d, d]
+  double* resid;       // [H] |Z Y - I|_F at exit, nullable
+};
+struct WhitenRowsArgs {
+  int H, d;
+  int64_t M;                        // rows per head
+  int64_t head_stride, row_stride;  // elements, shared by Y and Yw
+  const void* Y;
+  void* Yw;
+  const double* mu;  // [H, d]
+  const double* W;   // [H, d, d]
+};
+int whiten_blocks(int H, int N);
+size_t whiten_fit_ws_bytes(int H, int N, int d);
+hipError_t launch_whiten_fit(WhitenFitArgs a, int dtype, hipStream_t s);
+hipError_t launch_whiten_rows(const WhitenRowsArgs& a, int dtype, hipStream_t s);
 
 // ---- centroid inverse norms -------------------------------------------------
 hipError_t launch_inv_norms(int dtype, int H, int K, int d, const void* C, float* cinv,

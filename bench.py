@@ -102,8 +102,9 @@ def parse():
                    help="run one plain device copy (256 MiB read, 256 MiB written) before the "
                         "timed region, as the reference kernel for HBM byte counters")
     p.add_argument("--workload", default="batched_decode",
-                   choices=("batched_decode", "layer_decode", "layer_decode_hier", "prefix_states",
-                            "prefix_states_streamed", "memory_build"),
+                   choices=("batched_decode", "batched_decode_whitened", "layer_decode",
+                            "layer_decode_hier", "prefix_states", "prefix_states_streamed",
+                            "memory_build"),
                    help="batched_decode (the headline metric) or one of the offline build "
                         "workloads, reported on their MFMA rooflines")
     return p.parse_args()
@@ -120,6 +121,9 @@ def main():
         return
     if args.workload == "layer_decode_hier":
         run_layers_hier(args)
+        return
+    if args.workload == "batched_decode_whitened":
+        run_whitened(args)
         return
     if args.workload != "batched_decode":
         run_build(args)
@@ -244,6 +248,113 @@ def main():
     # ---- CPU baseline: the fp64 oracle, bounded sample of the same workload
     if args.cpu_seconds > 0:
         result["cpu_baseline"] = cpu_baseline(inp0, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def run_whitened(args, n_calib=16384):
+    """The batched-decode workload with whitening at retrieval: per head a
+    transform fit on 16384 calibration queries (64-centre mixture), the
+    table whitened once, and every step whitening its queries before the
+    lookup.  Timed beside it in the same process: the plain step on the same
+    replicas."""
+    import torch
+    from attention_state_memory_amd import api, synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def to_dev(x):
+        x = np.ascontiguousarray(x)
+        if x.dtype == np.uint16:
+            return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(x).to(dev)
+
+    reps, host_inputs = [], []
+    fit_ms, rows_ms = [], []
+    for r in range(args.replicas):
+        inp = synth.batched_decode(r)
+        host_inputs.append(inp)
+        t = {k: to_dev(inp[k]) for k in ("q", "C", "Abar", "LSEbar", "Kl", "Vl", "kv_start", "kv_len")}
+        t["cinv"] = api.centroid_inv_norms(t["C"])
+        X = to_dev(synth.mixture_queries([8, r], inp["Hq"], n_calib, inp["d"], M=64))
+        ws_fit = torch.zeros(int(api.lib().asm_whiten_fit_ws(api.BF16, inp["Hq"], n_calib, inp["d"])),
+                             dtype=torch.uint8, device=dev)
+        fit_ms.append(_timed(lambda: api.whiten_fit(X, workspace=ws_fit), 1))
+        t["mu"], t["W"], _ = api.whiten_fit(X, workspace=ws_fit)
+        t["Cw"] = torch.empty_like(t["C"])
+        rows_ms.append(_timed(lambda: api.whiten_rows(t["C"], t["mu"], t["W"], out=t["Cw"]), 1))
+        t["cwinv"] = api.centroid_inv_norms(t["Cw"])
+        del X, ws_fit
+        reps.append(t)
+        print(f"replica {r} resident and whitened", file=sys.stderr, flush=True)
+    inp0 = host_inputs[0]
+    B, Hq, Hkv, d, K = inp0["B"], inp0["Hq"], inp0["Hkv"], inp0["d"], inp0["K"]
+    max_kv = 4096
+    code = api.BF16
+    ws_w = int(api.lib().asm_decode_step_whitened_ws(code, B, Hq, Hkv, d, K, max_kv))
+    ws = torch.zeros(ws_w, dtype=torch.uint8, device=dev)
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+    out_lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    out_idx = torch.empty((B, Hq), dtype=torch.int32, device=dev)
+
+    def step_whitened(t):
+        api.decode_step_whitened(t["q"], t["mu"], t["W"], t["Cw"], t["cwinv"], t["Abar"],
+                                 t["LSEbar"], t["Kl"], t["Vl"], t["kv_start"], t["kv_len"], max_kv,
+                                 inp0["scale"], out=out, out_lse=out_lse, out_idx=out_idx,
+                                 workspace=ws)
+
+    def step_plain(t):
+        api.decode_step(t["q"], t["C"], t["cinv"], t["Abar"], t["LSEbar"], t["Kl"], t["Vl"],
+                        t["kv_start"], t["kv_len"], max_kv, inp0["scale"], out=out,
+                        out_lse=out_lse, out_idx=out_idx, workspace=ws)
+
+    def graph_ms(step):
+        stream = torch.cuda.Stream(dev)
+        with torch.cuda.stream(stream):
+            for i in range(args.warmup):
+                step(reps[i % len(reps)])
+        stream.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for t in reps:
+                step(t)
+        n = max(1, args.steps // len(reps))
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            g.replay()
+            e0.record(stream)
+            for _ in range(n):
+                g.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / (n * len(reps)), n * len(reps)
+
+    ms_w, steps = graph_ms(step_whitened)
+    ms_p, _ = graph_ms(step_plain)
+    alg_bytes = float(np.mean([algorithmic_bytes(h) for h in host_inputs]))
+    # plus what whitening adds per step: mu and W of every head (float64)
+    alg_bytes += Hq * (d + d * d) * 8
+    achieved = alg_bytes / (ms_w * 1e-3) / 1e9
+    result = {
+        "metric": "ASM decode queries/sec (heads x tokens) at K=8192 with whitening at retrieval",
+        "value": B * Hq / (ms_w * 1e-3), "unit": "head-queries/s", "n_gpus": 1,
+        "steps": steps, "warmup": args.warmup, "ms_per_step": ms_w, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (batched-decode inputs; whitening fit on 16384 seeded 64-centre "
+                "mixture queries per head)",
+        "config": {"workload": "batched_decode_whitened", "K": K, "batch": B, "q_heads": Hq,
+                   "kv_heads": Hkv, "head_dim": d, "local_len": "U{512..4096}",
+                   "calibration_queries": n_calib, "replicas": len(reps), "launch": "hip_graph"},
+        "plain_ms_per_step": ms_p,
+        "whitening_overhead_us": (ms_w - ms_p) * 1e3,
+        "fit_ms": float(np.mean(fit_ms)),
+        "table_whitening_ms": float(np.mean(rows_ms)),
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "algorithmic_bytes_per_step": alg_bytes,
+                     "timed": "HIP events around graph replays of asm_decode_step_whitened"},
+    }
     print(json.dumps(result), flush=True)
 
 

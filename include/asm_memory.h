@@ -60,7 +60,7 @@ enum asm_status_code {
 enum asm_dtype { ASM_BF16 = 0, ASM_F32 = 1 };
 
 /* ABI version of this header (bumped on any signature change). */
-#define ASM_ABI_VERSION 3
+#define ASM_ABI_VERSION 4
 int asm_abi_version(void);
 
 /* Static text for a status code. */
@@ -150,6 +150,50 @@ int asm_decode_step_hier(int dtype, int B, int Hq, int Hkv, int d, int K, int S,
                          const int32_t* kv_len, int max_kv_len, float* out, float* out_lse,
                          int32_t* out_idx, int32_t* out_probes, void* ws, size_t ws_bytes,
                          hipStream_t stream);
+
+/*
+ * Whitening at retrieval ([TS] Recuperación: the cosine lookup may run
+ * after a whitening transform).  The transform of head h is
+ * x -> W[h] (x - mu[h]), fit on that head's calibration queries:
+ *   mu = mean of the rows, Sigma = their population covariance plus
+ *   ridge * trace(Sigma) / d on the diagonal, W = Sigma^-1/2 (symmetric).
+ * Whitened rows are rounded once, to nearest-even, to the row type.
+ * d in {64, 128}; bf16 or float32 rows.
+ *
+ * asm_whiten_fit -- mu [H, d] and W [H, d, d] (float64) from X [H, N, d].
+ *   The inverse square root is the coupled Newton-Schulz iteration in
+ *   float64 (at most 100 rounds); resid [H] (float64, nullable) receives
+ *   |Z Y - I|_F at exit, about 1e-14 when it converged.  Needs N >= 1 and
+ *   ridge >= 0; with ridge = 0 the covariance must be positive definite.
+ *   Workspace: asm_whiten_fit_ws bytes.
+ * asm_whiten_rows -- Yw = round(W[h] (Y - mu[h])) for M rows of each of H
+ *   heads.  Row r of head h starts at element h*head_stride + r*row_stride
+ *   of Y and of Yw (the same layout); d contiguous elements per row.  Yw
+ *   must not overlap Y.  Whitening the memory table C [H, K, d] is
+ *   (M = K, head_stride = K*d, row_stride = d); its inverse norms come from
+ *   asm_centroid_inv_norms on the whitened table.
+ * asm_decode_step_whitened -- asm_decode_step whose lookup scores the
+ *   whitened query against the whitened table: q is whitened into the
+ *   workspace (as asm_whiten_rows), idx[b,h] = argmax_k qw.Cw[h,k] *
+ *   cwinv[h,k]; the local attention and the merge use the raw q.
+ *   Cw, cwinv: the whitened table and its inverse norms; other arguments as
+ *   asm_decode_step; workspace: asm_decode_step_whitened_ws bytes.
+ */
+size_t asm_whiten_fit_ws(int dtype, int H, int N, int d);
+int asm_whiten_fit(int dtype, int H, int N, int d, const void* X, double ridge, double* mu,
+                   double* W, double* resid, void* ws, size_t ws_bytes, hipStream_t stream);
+int asm_whiten_rows(int dtype, int H, int64_t M, int d, const void* Y, int64_t head_stride,
+                    int64_t row_stride, const double* mu, const double* W, void* Yw,
+                    hipStream_t stream);
+size_t asm_decode_step_whitened_ws(int dtype, int B, int Hq, int Hkv, int d, int K,
+                                   int max_kv_len);
+int asm_decode_step_whitened(int dtype, int B, int Hq, int Hkv, int d, int K, float scale,
+                             const void* q, const double* mu, const double* W, const void* Cw,
+                             const float* cwinv, const float* Abar, const float* LSEbar,
+                             const void* Kl, const void* Vl, int64_t kv_head_stride,
+                             int64_t kv_tok_stride, int64_t kv_capacity, const int32_t* kv_start,
+                             const int32_t* kv_len, int max_kv_len, float* out, float* out_lse,
+                             int32_t* out_idx, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * asm_build_states -- prefix attention states of the calibration queries
