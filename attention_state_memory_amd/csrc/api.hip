@@ -342,6 +342,7 @@ int asm_whiten_rows(int dtype, int H, int64_t M, int d, const void* Y, int64_t h
     return fail(ASM_ERR_SHAPE, "too many rows for one launch");
   if (!Y || !Yw || !mu || !W) return fail(ASM_ERR_NULL, "Y, Yw, mu and W are required");
   if (Y == Yw) return fail(ASM_ERR_SHAPE, "Yw must not alias Y");
+  if (reinterpret_cast<uintptr_t>(W) % 16 != 0) return fail(ASM_ERR_ALIGN, "W must be 16-byte aligned");
   asmk::WhitenRowsArgs a{};
   a.H = H; a.d = d; a.M = M; a.head_stride = head_stride; a.row_stride = row_stride;
   a.Y = Y; a.Yw = Yw; a.mu = mu; a.W = W;

@@ -24,8 +24,8 @@
 //                    Z converges to A^-1/2 (all eigenvalues of A are in
 //                    (0, 1]); W = Z / sqrt(|Sigma|_F), symmetrised;
 //   wh_rows          Yw = round(W (y - mu)) for rows y at any head and row
-//                    stride: a 16-output x 32-row tile per workgroup, the 16
-//                    rows of W and the 32 centred rows in LDS.
+//                    stride: 32 rows x 64 outputs per workgroup on the
+//                    float64 MFMA (16x16x4), operands staged in LDS.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -33,11 +33,11 @@ namespace asmk {
 
 namespace {
 
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
 constexpr int kThreads = 256;
 constexpr int kCovRows = 16;   // rows staged per pass of wh_cov_partial
 constexpr int kGemmK = 16;     // k-slab of the in-workgroup products
-constexpr int kRowsTile = 32;  // rows per wh_rows workgroup
-constexpr int kOutTile = 16;   // outputs per wh_rows workgroup
 
 template <typename T>
 __device__ __forceinline__ double load_d(const T* p, size_t i) {
@@ -256,39 +256,72 @@ __global__ void __launch_bounds__(kThreads) wh_invsqrt(WhitenFitArgs a) {
   if (t == 0 && a.resid) a.resid[h] = res;
 }
 
+// One workgroup per (head, 32 rows, 64 outputs); wave w owns outputs
+// [16 w, 16 w + 16) of the 64 for all 32 rows, as two 16 x 16 tiles on the
+// float64 matrix cores (16x16x4 per step, D/4 steps each).  The 32 centred
+// rows and each wave's 16 rows of W are first staged in LDS with coalesced
+// loads.  Lane l supplies row / output l % 16 and k = 4 s + l / 16 at step s;
+// after the last step lane l holds rows l / 16 + 4 r (r = 0..3) of output
+// l % 16.
 template <typename T, int D>
 __global__ void __launch_bounds__(kThreads) wh_rows(WhitenRowsArgs a) {
-  __shared__ double ws_[kOutTile][D + 1];
-  __shared__ double ys[kRowsTile][D + 1];
-  const int nob = D / kOutTile;
-  const int rb = blockIdx.x / (a.H * nob);
-  const int rem = blockIdx.x % (a.H * nob);
-  const int h = rem / nob, ob = rem % nob;
-  const int t = threadIdx.x, to = t % kOutTile, rg = t / kOutTile;
-  const int64_t row0 = int64_t(rb) * kRowsTile;
-  const double* W = a.W + size_t(h) * D * D + size_t(ob) * kOutTile * D;
-  const double* mu = a.mu + size_t(h) * D;
+  constexpr int KL = D / 4;
+  constexpr int LD = D + 2;  // LDS row pitch (doubles)
+  constexpr int NG = D / 64;  // 64-output groups per head
+  __shared__ double wsm[4][16 * LD];
+  __shared__ double ysm[32 * LD];
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int g = blockIdx.x % NG;
+  const int h = (blockIdx.x / NG) % a.H;
+  const int64_t row0 = int64_t(blockIdx.x / NG / a.H) * 32;
+  // All staging loads are issued before the first LDS store (one round trip):
+  // thread t always covers dim t % D of rows t / D + (256 / D) j, and a row
+  // past M reads row M - 1 and stores 0.
+  constexpr int YE = 32 * D / kThreads;
+  constexpr int WE = 16 * D / 2 / 64;
+  const int o0 = g * 64 + w * 16;  // first output of this wave
+  const double* W = a.W + (size_t(h) * D + o0) * D;
+  double2 wv[WE];
+#pragma unroll
+  for (int j = 0; j < WE; ++j) wv[j] = *reinterpret_cast<const double2*>(W + 2 * (lane + 64 * j));
   const T* Y = static_cast<const T*>(a.Y);
-  for (int e = t; e < kOutTile * D; e += kThreads) ws_[e / D][e % D] = W[e];
-  for (int e = t; e < kRowsTile * D; e += kThreads) {
+  const int k_t = t % D, r_t = t / D;
+  const double mu_t = a.mu[size_t(h) * D + k_t];
+  T yv[YE];  // raw elements: converted only after every load is issued
+#pragma unroll
+  for (int j = 0; j < YE; ++j) {
+    const int64_t row = row0 + r_t + (kThreads / D) * j;
+    const int64_t rc = row < a.M ? row : a.M - 1;
+    yv[j] = Y[size_t(h * a.head_stride + rc * a.row_stride + k_t)];
+  }
+#pragma unroll
+  for (int j = 0; j < YE; ++j) {
+    const int r = r_t + (kThreads / D) * j;
+    ysm[r * LD + k_t] = row0 + r < a.M ? load_d(yv, j) - mu_t : 0.0;
+  }
+#pragma unroll
+  for (int j = 0; j < WE; ++j) {
+    const int e = 2 * (lane + 64 * j);
     const int r = e / D, k = e % D;
-    const int64_t row = row0 + r;
-    ys[r][k] = row < a.M ? load_d(Y, size_t(h * a.head_stride + row * a.row_stride + k)) - mu[k]
-                         : 0.0;
+    wsm[w][r * LD + k] = wv[j].x;
+    wsm[w][r * LD + k + 1] = wv[j].y;
   }
   __syncthreads();
-  double acc[kRowsTile / 16] = {};
-  for (int k = 0; k < D; ++k) {
-    const double w = ws_[to][k];
-#pragma unroll
-    for (int j = 0; j < kRowsTile / 16; ++j) acc[j] = fma(w, ys[rg + 16 * j][k], acc[j]);
+  const int i = lane % 16, kq = lane / 16;
+  f64x4 c0 = {0.0, 0.0, 0.0, 0.0}, c1 = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll 8
+  for (int s = 0; s < KL; ++s) {
+    const int k = 4 * s + kq;
+    const double b = wsm[w][i * LD + k];
+    c0 = __builtin_amdgcn_mfma_f64_16x16x4f64(ysm[i * LD + k], b, c0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_f64_16x16x4f64(ysm[(16 + i) * LD + k], b, c1, 0, 0, 0);
   }
   T* Yw = static_cast<T*>(a.Yw);
 #pragma unroll
-  for (int j = 0; j < kRowsTile / 16; ++j) {
-    const int64_t row = row0 + rg + 16 * j;
-    if (row < a.M)
-      store_round(Yw, size_t(h * a.head_stride + row * a.row_stride + ob * kOutTile + to), acc[j]);
+  for (int r = 0; r < 4; ++r) {
+    const int64_t ra = row0 + kq + 4 * r, rb = ra + 16;
+    if (ra < a.M) store_round(Yw, size_t(h * a.head_stride + ra * a.row_stride + o0 + i), c0[r]);
+    if (rb < a.M) store_round(Yw, size_t(h * a.head_stride + rb * a.row_stride + o0 + i), c1[r]);
   }
 }
 
@@ -333,8 +366,7 @@ hipError_t launch_whiten_fit(WhitenFitArgs a, int dtype, hipStream_t s) {
 
 hipError_t launch_whiten_rows(const WhitenRowsArgs& a, int dtype, hipStream_t s) {
   if (a.M == 0) return hipSuccess;
-  const int64_t rblocks = (int64_t(a.M) + kRowsTile - 1) / kRowsTile;
-  const dim3 grid(unsigned(rblocks * a.H * (a.d / kOutTile)));
+  const dim3 grid(unsigned((int64_t(a.M) + 31) / 32 * a.H * (a.d / 64)));
   if (a.d == 128) {
     if (dtype == 0)
       hipLaunchKernelGGL((wh_rows<uint16_t, 128>), grid, dim3(kThreads), 0, s, a);

@@ -169,7 +169,7 @@ int asm_decode_step_hier(int dtype, int B, int Hq, int Hkv, int d, int K, int S,
  * asm_whiten_rows -- Yw = round(W[h] (Y - mu[h])) for M rows of each of H
  *   heads.  Row r of head h starts at element h*head_stride + r*row_stride
  *   of Y and of Yw (the same layout); d contiguous elements per row.  Yw
- *   must not overlap Y.  Whitening the memory table C [H, K, d] is
+ *   must not overlap Y; W must be 16-byte aligned.  Whitening the memory table C [H, K, d] is
  *   (M = K, head_stride = K*d, row_stride = d); its inverse norms come from
  *   asm_centroid_inv_norms on the whitened table.
  * asm_decode_step_whitened -- asm_decode_step whose lookup scores the
