@@ -101,6 +101,10 @@ def parse():
     p.add_argument("--copy-calibration", action="store_true",
                    help="run one plain device copy (256 MiB read, 256 MiB written) before the "
                         "timed region, as the reference kernel for HBM byte counters")
+    p.add_argument("--K", type=int, default=8192, help="layer_decode_hier: entries per head")
+    p.add_argument("--supers", type=int, default=128, help="layer_decode_hier: super-centroids S")
+    p.add_argument("--probes", type=int, default=8, help="layer_decode_hier: probes p")
+    p.add_argument("--layers", type=int, default=32, help="layer_decode_hier: layers in the graph")
     p.add_argument("--workload", default="batched_decode",
                    choices=("batched_decode", "batched_decode_whitened", "layer_decode",
                             "layer_decode_hier", "prefix_states", "prefix_states_streamed",
@@ -487,10 +491,10 @@ def run_layers(args):
 # batch-1 decode through 32 layers at K=8192: two-level lookup against flat
 # --------------------------------------------------------------------------
 
-def run_layers_hier(args, S=128, p=8, layers=32):
-    """Batch-1 decode through 32 layers with K=8192 entries per query head,
-    once with the flat search and once with the two-level lookup (S=128
-    supers, p=8 probes).  The entries are clusterable (64-centre mixture
+def run_layers_hier(args):
+    """Batch-1 decode through `--layers` layers (32) with `--K` entries per
+    query head (8192), once with the flat search and once with the two-level
+    lookup (`--supers` S = 128, `--probes` p = 8).  The entries are clusterable (64-centre mixture
     queries per head, as a built memory's are) and every layer's query is an
     entry plus noise.  Reports per-layer time of both lookups and the
     two-level lookup's recall@1 against the flat search."""
@@ -506,7 +510,7 @@ def run_layers_hier(args, S=128, p=8, layers=32):
             return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
         return torch.from_numpy(x).to(dev)
 
-    K, Hq = 8192, 32
+    K, S, p, layers, Hq = args.K, args.supers, args.probes, args.layers, 32
     L = []
     for l in range(layers):
         inp = synth.decode_inputs([6, l], B=1, Hq=Hq, Hkv=8, d=128, K=K, kv_lens=[2048])
@@ -521,6 +525,7 @@ def run_layers_hier(args, S=128, p=8, layers=32):
         t["cinv"] = api.centroid_inv_norms(t["C"])
         t["index"] = api.build_index(t["C"], S, 4)
         L.append(t)
+        print(f"layer {l} resident", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     print("layers and indices resident", file=sys.stderr, flush=True)
     scale = synth.softmax_scale(128)
@@ -576,7 +581,8 @@ def run_layers_hier(args, S=128, p=8, layers=32):
                                  + (128 * 4 + 4) + (128 * 4 + 8)) + 8 * 2048 * 128 * 2 * 2 + 8)
     gbs = hier_bytes / (ms_hier * 1e-3) / 1e9
     result = {
-        "metric": "ASM decode, batch 1 through 32 layers at K=8192, two-level lookup: per-layer latency",
+        "metric": f"ASM decode, batch 1 through {layers} layers at K={K}, two-level lookup: "
+                  "per-layer latency",
         "value": ms_hier * 1e3 / layers, "unit": "us/layer", "n_gpus": 1, "steps": reps,
         "warmup": args.warmup, "ms_per_step": ms_hier, "higher_is_better": False,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
@@ -591,7 +597,7 @@ def run_layers_hier(args, S=128, p=8, layers=32):
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS, "traffic": None,
                      "algorithmic_bytes_per_step": hier_bytes,
-                     "timed": "HIP events around replays of one graph holding the 32 layers' "
+                     "timed": "HIP events around replays of one graph holding the layers' "
                               "asm_decode_step_hier calls"},
     }
     print(json.dumps(result), flush=True)
