@@ -55,6 +55,8 @@ SIGNATURES = {
     "asm_build_states_streamed_ws": (_c_size, [_c_int] * 6),
     "asm_build_states_streamed": (_c_int, [_c_int] * 7 + [_c_float, _vp, _vp, _vp, _vp, _vp,
                                                           _c_int, _vp, _c_size, _vp, _vp]),
+    "asm_build_memory_ws": (_c_size, [_c_int] * 5),
+    "asm_build_memory": (_c_int, [_c_int] * 6 + [_vp] * 9 + [_vp, _c_size, _vp]),
     "asm_build_index_ws": (_c_size, [_c_int] * 5),
     "asm_build_index": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                  _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_size, _vp]),
@@ -398,24 +400,30 @@ def aggregate(X, idx, C, *, A=None, LSE=None, cinv=None, count=None, Abar=None, 
     return C, cinv, count, Abar, LSEbar
 
 
-def build_memory(X, K: int, iters: int, A=None, LSE=None):
+def build_memory(X, K: int, iters: int, A=None, LSE=None, *, workspace=None):
     """Cosine k-means with first-K initialisation followed by the state
-    aggregation of the final partition: `iters` >= 1 rounds of
-    kmeans_assign + aggregate; the last aggregate also merges the states
+    aggregation of the final partition (asm_build_memory): `iters` >= 1
+    rounds of assignment and mean; the last round also merges the states
     (A, LSE) when they are given.  Returns (C, cinv, count, idx, Abar, LSEbar)."""
-    if iters < 1:
-        raise ValueError("iters must be >= 1")
+    _dev(X, "X")
+    code = _dtype_code(X)
     H, N, d = X.shape
-    C = X[:, :K, :].clone()
-    cinv = centroid_inv_norms(C)
-    idx = torch.empty((H, N), dtype=torch.int32, device=X.device)
-    count = torch.empty((H, K), dtype=torch.int32, device=X.device)
+    dev = X.device
+    C = torch.empty((H, K, d), dtype=X.dtype, device=dev)
+    cinv = torch.empty((H, K), dtype=torch.float32, device=dev)
+    idx = torch.empty((H, N), dtype=torch.int32, device=dev)
+    count = torch.empty((H, K), dtype=torch.int32, device=dev)
     Abar = LSEbar = None
-    for t in range(iters):
-        kmeans_assign(X, C, cinv, idx=idx)
-        last = t == iters - 1 and A is not None
-        _, _, _, Abar, LSEbar = aggregate(X, idx, C, A=A, LSE=LSE, cinv=cinv, count=count,
-                                          with_states=last)
+    if A is not None:
+        _dev(A, "A", torch.float32)
+        _dev(LSE, "LSE", torch.float32)
+        Abar = torch.empty((H, K, d), dtype=torch.float32, device=dev)
+        LSEbar = torch.empty((H, K), dtype=torch.float32, device=dev)
+    nbytes = int(lib().asm_build_memory_ws(code, H, N, int(K), d))
+    ws = _workspace(nbytes, dev, workspace)
+    _check("asm_build_memory", lib().asm_build_memory(
+        code, H, N, int(K), d, int(iters), _ptr(X), _ptr(A), _ptr(LSE), _ptr(C), _ptr(cinv),
+        _ptr(Abar), _ptr(LSEbar), _ptr(count), _ptr(idx), _ptr(ws), nbytes, _stream(dev)))
     return C, cinv, count, idx, Abar, LSEbar
 
 

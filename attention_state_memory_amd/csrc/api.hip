@@ -619,6 +619,48 @@ int asm_aggregate(int dtype, int H, int N, int K, int d, const void* X, const in
 }
 
 // ---------------------------------------------------------------------------
+size_t asm_build_memory_ws(int dtype, int H, int N, int K, int d) {
+  const size_t a = asm_kmeans_assign_ws(dtype, H, N, K, d);
+  const size_t g = asm_aggregate_ws(dtype, H, N, K, d);
+  if (check_dtype(dtype) != ASM_OK || check_d(dtype, d) != ASM_OK || H < 1 || K < 1 || N < K)
+    return 0;
+  return a > g ? a : g;
+}
+
+int asm_build_memory(int dtype, int H, int N, int K, int d, int iters, const void* X,
+                     const float* A, const float* LSE, void* C, float* cinv, float* Abar,
+                     float* LSEbar, int32_t* count, int32_t* idx, void* ws, size_t ws_bytes,
+                     hipStream_t stream) {
+  ASM_TRY(check_dtype(dtype));
+  ASM_TRY(check_d(dtype, d));
+  if (H < 1 || K < 1 || N < K || iters < 1)
+    return fail(ASM_ERR_SHAPE, "need H, K >= 1, N >= K and iters >= 1 (H=%d N=%d K=%d iters=%d)",
+                H, N, K, iters);
+  if (!X || !C || !cinv || !count || !idx)
+    return fail(ASM_ERR_NULL, "X, C, cinv, count and idx are required");
+  if ((A == nullptr) != (LSE == nullptr) || (Abar == nullptr) != (A == nullptr) ||
+      (LSEbar == nullptr) != (A == nullptr))
+    return fail(ASM_ERR_NULL, "A, LSE, Abar and LSEbar must all be given or all be NULL");
+  ASM_TRY(check_bf16_ptrs(dtype, {X, C}));
+  ASM_TRY(check_ws(ws, ws_bytes, asm_build_memory_ws(dtype, H, N, K, d)));
+  // first-K initialisation: C[h] = X[h, :K]
+  const size_t esz = dtype == ASM_BF16 ? 2 : 4;
+  ASM_TRY(hip_status(hipMemcpy2DAsync(C, size_t(K) * d * esz, X, size_t(N) * d * esz,
+                                      size_t(K) * d * esz, size_t(H), hipMemcpyDeviceToDevice,
+                                      stream),
+                     "copy initial centroids"));
+  ASM_TRY(asm_centroid_inv_norms(dtype, H, K, d, C, cinv, stream));
+  for (int t = 0; t < iters; ++t) {
+    const bool last = t == iters - 1;
+    ASM_TRY(asm_kmeans_assign(dtype, H, N, K, d, X, C, cinv, idx, nullptr, ws, ws_bytes, stream));
+    ASM_TRY(asm_aggregate(dtype, H, N, K, d, X, idx, last ? A : nullptr, last ? LSE : nullptr, C,
+                          cinv, count, last ? Abar : nullptr, last ? LSEbar : nullptr, ws, ws_bytes,
+                          stream));
+  }
+  return ok();
+}
+
+// ---------------------------------------------------------------------------
 static size_t build_index_ws_bytes(int H, int K, int S) {
   size_t off = asmk::align_up(size_t(H) * K * sizeof(int32_t), kAlign);  // entry -> super
   off += asmk::align_up(size_t(H) * S * sizeof(int32_t), kAlign);        // scatter cursors

@@ -202,22 +202,25 @@ def main():
             graph.replay()
         stream.synchronize()
 
-    steps = args.steps if graph is None else max(R, (args.steps // R) * R)
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
+    steps = max(R, (args.steps // R) * R)
+    # one event per group of R steps (one graph replay) for the spread
+    groups = steps // R
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(groups + 1)]
     torch.cuda.synchronize()
     with torch.cuda.stream(stream):
-        e0.record(stream)
-        if graph is None:
-            for i in range(steps):
-                calls[i % R]()
-        else:
-            for _ in range(steps // R):
+        evs[0].record(stream)
+        for gi in range(groups):
+            if graph is None:
+                for i in range(R):
+                    calls[i]()
+            else:
                 graph.replay()
-        e1.record(stream)
+            evs[gi + 1].record(stream)
     torch.cuda.synchronize()
-    ms_total = e0.elapsed_time(e1)
-    ms_step = ms_total / steps
+    ms_total = evs[0].elapsed_time(evs[-1])
+    ms_step = ms_total / (groups * R)
+    steps = groups * R
+    per_step = np.array([evs[i].elapsed_time(evs[i + 1]) / R for i in range(groups)])
     queries = B * Hq
     qps = queries / (ms_step * 1e-3)
     alg_bytes = float(np.mean([algorithmic_bytes(h) for h in host_inputs]))
@@ -240,6 +243,7 @@ def main():
         "config": {"workload": "batched_decode", "K": K, "batch": B, "q_heads": Hq,
                    "kv_heads": Hkv, "head_dim": d, "local_len": "U{512..4096}",
                    "replicas": R, "launch": "eager" if graph is None else "hip_graph"},
+        "ms_per_step_p10_p50_p90": [float(np.percentile(per_step, q)) for q in (10, 50, 90)],
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic["bytes_per_step"] if traffic else None,

@@ -60,7 +60,7 @@ enum asm_status_code {
 enum asm_dtype { ASM_BF16 = 0, ASM_F32 = 1 };
 
 /* ABI version of this header (bumped on any signature change). */
-#define ASM_ABI_VERSION 4
+#define ASM_ABI_VERSION 5
 int asm_abi_version(void);
 
 /* Static text for a status code. */
@@ -288,6 +288,25 @@ size_t asm_aggregate_ws(int dtype, int H, int N, int K, int d);
 int asm_aggregate(int dtype, int H, int N, int K, int d, const void* X, const int32_t* idx,
                   const float* A, const float* LSE, void* C, float* cinv, int32_t* count,
                   float* Abar, float* LSEbar, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * asm_build_memory -- the whole table build ([TS] Agrupamiento then
+ * Agregación) in one call: C[h] = X[h, :K] (first-K initialisation), its
+ * inverse norms, then `iters` rounds of asm_kmeans_assign and the mean step
+ * of asm_aggregate; the last round also aggregates the states when A and
+ * LSE are given.  The same results as that sequence of calls.
+ *   X [H, N, d] dtype with N >= K; A [H, N, d], LSE [H, N] float32
+ *   (nullable together with Abar, LSEbar).
+ *   Outputs: C [H, K, d] dtype; cinv [H, K] float32; count [H, K] int32 (of
+ *   the last partition); idx [H, N] int32 (the last partition); Abar
+ *   [H, K, d], LSEbar [H, K] float32.
+ *   Workspace: asm_build_memory_ws bytes.
+ */
+size_t asm_build_memory_ws(int dtype, int H, int N, int K, int d);
+int asm_build_memory(int dtype, int H, int N, int K, int d, int iters, const void* X,
+                     const float* A, const float* LSE, void* C, float* cinv, float* Abar,
+                     float* LSEbar, int32_t* count, int32_t* idx, void* ws, size_t ws_bytes,
+                     hipStream_t stream);
 
 /*
  * asm_build_index -- the two-level index used by asm_decode_step_hier.  For

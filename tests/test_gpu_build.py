@@ -210,3 +210,32 @@ def test_tiny_build_and_decode_teacher_forced():
     ref, ref_lse = O.decode_with_idx(q64, di, host(Abar).astype(np.float64),
                                      host(LSEbar).astype(np.float64), ks, vs, t["scale"])
     assert_states_close(host(out), host(lse), ref, ref_lse)
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64)])
+def test_build_memory_equals_the_call_sequence(dtype, d):
+    """asm_build_memory gives the same bits as first-K initialisation,
+    centroid_inv_norms and `iters` rounds of kmeans_assign + aggregate."""
+    r = _rng(9, d)
+    H, N, K, iters = 3, 700, 50, 3
+    X = synth.mixture_queries([230, d], H, N, d, M=16, dtype=dtype)
+    A = r.standard_normal((H, N, d)).astype(np.float32)
+    LSE = r.uniform(5, 12, (H, N)).astype(np.float32)
+    Xd, Ad, Ld = dev(X), dev(A), dev(LSE)
+    got = api.build_memory(Xd, K, iters, Ad, Ld)
+    C = Xd[:, :K, :].clone()
+    cinv = api.centroid_inv_norms(C)
+    idx = torch.empty((H, N), dtype=torch.int32, device="cuda")
+    count = torch.empty((H, K), dtype=torch.int32, device="cuda")
+    for t in range(iters):
+        api.kmeans_assign(Xd, C, cinv, idx=idx)
+        _, _, _, Abar, LSEbar = api.aggregate(Xd, idx, C, A=Ad, LSE=Ld, cinv=cinv, count=count,
+                                              with_states=t == iters - 1)
+    torch.cuda.synchronize()
+    for g, w in zip(got, (C, cinv, count, idx, Abar, LSEbar)):
+        assert np.array_equal(host(g), host(w), equal_nan=True)
+    # without states: no aggregation outputs, same table
+    C2, _, _, idx2, Ab2, Lb2 = api.build_memory(Xd, K, iters)
+    torch.cuda.synchronize()
+    assert Ab2 is None and Lb2 is None
+    assert np.array_equal(host(C2), host(C)) and np.array_equal(host(idx2), host(idx))
