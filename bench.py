@@ -118,7 +118,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; "
-                                   "multi-GPU runs are not part of this build"}))
+                                   "no multi-GPU mode"}))
         sys.exit(2)
     if args.workload == "layer_decode":
         run_layers(args)
