@@ -215,61 +215,57 @@ __global__ void __launch_bounds__(256) agg_finalize(AggregateArgs a) {
   if (lane == 0) a.LSEbar[item] = float(double(mx) + log(z) - log(double(n)));
 }
 
-// One wave per (head, cluster) for bf16 queries with d in {64, 128}.  The
-// member rows are loaded many at a time: one load brings 64 member indices,
-// then batches of member rows go out together (a row is D/8 lanes of 16
-// bytes, so one instruction covers 64*8/D rows) before the float64 sums.
-// Members beyond 64 are taken in further blocks of 64.
+// bf16 queries with d in {64, 128}: one group of D/8 lanes per (head,
+// cluster), 64*8/D clusters per wave, so that one wave's three dependent
+// memory rounds (member range, member list, member rows) serve several
+// clusters at once.  Lane `sub` of a group owns dims 8*sub .. 8*sub+7 of
+// the cluster: it sums them over all members in float64 (eight member rows
+// in flight), rounds the mean once, and for the states weighs the members'
+// a rows (two 16-byte pieces per lane) by Z.
 template <int D>
 __global__ void __launch_bounds__(256) agg_finalize_bf16(AggregateArgs a) {
-  constexpr int LPR = D / 8;       // lanes per query row
-  constexpr int RG = 64 / LPR;     // query rows per load instruction
-  constexpr int XBATCH = 4;        // query-row loads in flight
-  constexpr int ALPR = D / 4;      // lanes per state row (float32)
-  constexpr int ARG = 64 / ALPR;   // state rows per load instruction
-  constexpr int ABATCH = 4;        // state loads in flight
+  constexpr int LG = D / 8;   // lanes per cluster
+  constexpr int NG = 64 / LG;  // clusters per wave
+  constexpr int XB = 8;        // member rows in flight per group
   const int lane = threadIdx.x & 63;
-  const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (item >= a.H * a.K) return;
-  const int h = item / a.K;
-  const int32_t* off = a.offsets + size_t(h) * (a.K + 1) + (item - h * a.K);
+  const int g = lane / LG, sub = lane % LG, g0 = g * LG;
+  const int64_t item = (int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6)) * NG + g;
+  const bool live = item < int64_t(a.H) * a.K;
+  const int64_t it = live ? item : 0;
+  const int h = int(it / a.K);
+  const int32_t* off = a.offsets + size_t(h) * (a.K + 1) + (it - int64_t(h) * a.K);
   const int beg = off[0];
-  const int n = off[1] - beg;
+  const int n = live ? off[1] - beg : 0;
   const int32_t* mem = a.perm + size_t(h) * a.N + beg;
   const auto rx = make_rsrc(static_cast<const uint16_t*>(a.X) + size_t(h) * a.N * D, uint32_t(a.N) * D * 2);
-  const int sub = lane % LPR, rg = lane / LPR;
-  uint16_t* Crow = static_cast<uint16_t*>(a.C) + size_t(item) * D;
+  const int x_oob = int(uint32_t(a.N) * D * 2);
+  uint16_t* Crow = static_cast<uint16_t*>(a.C) + size_t(it) * D + 8 * sub;
 
   // ---- centroid: float64 sum of the members, one rounding to bf16
   double c[8];
   if (n > 0) {
     double sum[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
-    for (int m0 = 0; m0 < n; m0 += 64) {
-      const int cnt = min(64, n - m0);
-      const int myi = lane < cnt ? mem[m0 + lane] : 0;
-      for (int b0 = 0; b0 < cnt; b0 += XBATCH * RG) {
-        u32x4 v[XBATCH];
+    for (int m0 = 0; m0 < n; m0 += LG) {
+      const int cnt = min(LG, n - m0);
+      const int myi = sub < cnt ? mem[m0 + sub] : 0;
+      for (int b0 = 0; b0 < cnt; b0 += XB) {
+        u32x4 v[XB];
 #pragma unroll
-        for (int it = 0; it < XBATCH; ++it) {
-          const int mm = b0 + it * RG + rg;
-          const int row = __shfl(myi, mm & 63, 64);
+        for (int j = 0; j < XB; ++j) {
+          const int mm = b0 + j;
+          const int row = __shfl(myi, g0 + (mm & (LG - 1)), 64);
           // members past cnt read from past the buffer end: zeros, no traffic
-          const int voff = mm < cnt ? (row * D + 8 * sub) * 2 : int(uint32_t(a.N) * D * 2);
-          v[it] = buf16(rx, voff, 0);
+          v[j] = buf16(rx, mm < cnt ? (row * D + 8 * sub) * 2 : x_oob, 0);
         }
 #pragma unroll
-        for (int it = 0; it < XBATCH; ++it)
+        for (int j = 0; j < XB; ++j)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            sum[2 * e] += double(bf16_lo(v[it][e]));
-            sum[2 * e + 1] += double(bf16_hi(v[it][e]));
+            sum[2 * e] += double(bf16_lo(v[j][e]));
+            sum[2 * e + 1] += double(bf16_hi(v[j][e]));
           }
       }
     }
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-#pragma unroll
-      for (int m = LPR; m < 64; m <<= 1) sum[e] += __shfl_xor(sum[e], m, 64);
     u32x4 packed;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -279,9 +275,9 @@ __global__ void __launch_bounds__(256) agg_finalize_bf16(AggregateArgs a) {
       c[2 * e] = double(bf16_lo(packed[e]));
       c[2 * e + 1] = double(bf16_hi(packed[e]));
     }
-    if (rg == 0) *reinterpret_cast<u32x4*>(Crow + 8 * sub) = packed;
+    *reinterpret_cast<u32x4*>(Crow) = packed;
   } else {
-    const u32x4 packed = *reinterpret_cast<const u32x4*>(Crow + 8 * sub);
+    const u32x4 packed = *reinterpret_cast<const u32x4*>(Crow);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       c[2 * e] = double(bf16_lo(packed[e]));
@@ -292,62 +288,65 @@ __global__ void __launch_bounds__(256) agg_finalize_bf16(AggregateArgs a) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) ss = fma(c[e], c[e], ss);
 #pragma unroll
-  for (int m = 1; m < LPR; m <<= 1) ss += __shfl_xor(ss, m, 64);
-  if (lane == 0) a.cinv[item] = ss > 0.0 ? float(1.0 / sqrt(ss)) : 0.0f;
+  for (int m = 1; m < LG; m <<= 1) ss += __shfl_xor(ss, m, 64);
+  if (live && sub == 0) a.cinv[it] = ss > 0.0 ? float(1.0 / sqrt(ss)) : 0.0f;
 
-  if (a.Abar == nullptr) return;
+  if (a.Abar == nullptr || !live) return;
   // ---- state: Z-weighted mean of the members' a, mean of their Z
-  float* ab = a.Abar + size_t(item) * D;
+  float* ab = a.Abar + size_t(it) * D + 8 * sub;
   const float* LSE = a.LSE + size_t(h) * a.N;
   const auto ra = make_rsrc(a.A + size_t(h) * a.N * D, uint32_t(a.N) * D * 4);
-  const int asub = lane % ALPR, arg = lane / ALPR;
+  const int a_oob = int(uint32_t(a.N) * D * 4);
   float mx = -INFINITY;
-  for (int m = lane; m < n; m += 64) mx = fmaxf(mx, LSE[mem[m]]);
+  for (int m = sub; m < n; m += LG) mx = fmaxf(mx, LSE[mem[m]]);
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) mx = fmaxf(mx, __shfl_xor(mx, m, 64));
+  for (int m = 1; m < LG; m <<= 1) mx = fmaxf(mx, __shfl_xor(mx, m, 64));
   if (n == 0 || mx == -INFINITY) {
-    if (lane < ALPR) *reinterpret_cast<f32x4*>(ab + 4 * asub) = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (lane == 0) a.LSEbar[item] = -INFINITY;
+    reinterpret_cast<f32x4*>(ab)[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+    reinterpret_cast<f32x4*>(ab)[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (sub == 0) a.LSEbar[it] = -INFINITY;
     return;
   }
-  double z = 0.0, acc[4] = {0.0, 0.0, 0.0, 0.0};
-  for (int m0 = 0; m0 < n; m0 += 64) {
-    const int cnt = min(64, n - m0);
-    const int myi = lane < cnt ? mem[m0 + lane] : 0;
-    const float li = lane < cnt ? LSE[myi] : -INFINITY;
+  double z = 0.0, acc[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+  for (int m0 = 0; m0 < n; m0 += LG) {
+    const int cnt = min(LG, n - m0);
+    const int myi = sub < cnt ? mem[m0 + sub] : 0;
+    const float li = sub < cnt ? LSE[myi] : -INFINITY;
     const double wl = li == -INFINITY ? 0.0 : exp(double(li) - double(mx));
     z += wl;
-    for (int b0 = 0; b0 < cnt; b0 += ABATCH * ARG) {
-      u32x4 v[ABATCH];
+    for (int b0 = 0; b0 < cnt; b0 += XB / 2) {
+      u32x4 v[XB / 2][2];
 #pragma unroll
-      for (int it = 0; it < ABATCH; ++it) {
-        const int mm = b0 + it * ARG + arg;
-        const int row = __shfl(myi, mm & 63, 64);
-        const int voff = mm < cnt ? (row * D + 4 * asub) * 4 : int(uint32_t(a.N) * D * 4);
-        v[it] = buf16(ra, voff, 0);
+      for (int j = 0; j < XB / 2; ++j) {
+        const int mm = b0 + j;
+        const int row = __shfl(myi, g0 + (mm & (LG - 1)), 64);
+        const int voff = mm < cnt ? (row * D + 8 * sub) * 4 : a_oob;
+        v[j][0] = buf16(ra, voff, 0);
+        v[j][1] = buf16(ra, voff, 16);
       }
 #pragma unroll
-      for (int it = 0; it < ABATCH; ++it) {
-        const int mm = b0 + it * ARG + arg;
-        const double wgt = __shfl(wl, mm & 63, 64);  // 0 past cnt
+      for (int j = 0; j < XB / 2; ++j) {
+        const int mm = b0 + j;
+        const double wgt = __shfl(wl, g0 + (mm & (LG - 1)), 64);  // 0 past cnt
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[e] = fma(wgt, double(__uint_as_float(v[it][e])), acc[e]);
+        for (int e = 0; e < 4; ++e) {
+          acc[e] = fma(wgt, double(__uint_as_float(v[j][0][e])), acc[e]);
+          acc[4 + e] = fma(wgt, double(__uint_as_float(v[j][1][e])), acc[4 + e]);
+        }
       }
     }
   }
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) z += __shfl_xor(z, m, 64);
+  for (int m = 1; m < LG; m <<= 1) z += __shfl_xor(z, m, 64);
+  f32x4 o0, o1;
 #pragma unroll
-  for (int e = 0; e < 4; ++e)
-#pragma unroll
-    for (int m = ALPR; m < 64; m <<= 1) acc[e] += __shfl_xor(acc[e], m, 64);
-  if (lane < ALPR) {
-    f32x4 o;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) o[e] = float(acc[e] / z);
-    *reinterpret_cast<f32x4*>(ab + 4 * asub) = o;
+  for (int e = 0; e < 4; ++e) {
+    o0[e] = float(acc[e] / z);
+    o1[e] = float(acc[4 + e] / z);
   }
-  if (lane == 0) a.LSEbar[item] = float(double(mx) + log(z) - log(double(n)));
+  reinterpret_cast<f32x4*>(ab)[0] = o0;
+  reinterpret_cast<f32x4*>(ab)[1] = o1;
+  if (sub == 0) a.LSEbar[it] = float(double(mx) + log(z) - log(double(n)));
 }
 
 hipError_t launch_aggregate(const AggregateArgs& a, int dtype, hipStream_t s) {
@@ -360,10 +359,13 @@ hipError_t launch_aggregate(const AggregateArgs& a, int dtype, hipStream_t s) {
   if (HN > 0) hipLaunchKernelGGL(agg_scatter, grid_for(HN), dim3(256), 0, s, a);
   const dim3 fgrid(unsigned((HK + 3) / 4));
   const bool fits = int64_t(a.N) * a.d * 4 < (int64_t(1) << 31);
+  // the bf16 kernel serves 64*8/d clusters per wave, four waves per block
+  const int64_t cpb = int64_t(4) * (64 * 8 / (a.d > 0 ? a.d : 1));
+  const dim3 ggrid(unsigned((HK + cpb - 1) / cpb));
   if (dtype == 0 && a.d == 128 && fits)
-    hipLaunchKernelGGL(agg_finalize_bf16<128>, fgrid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL(agg_finalize_bf16<128>, ggrid, dim3(256), 0, s, a);
   else if (dtype == 0 && a.d == 64 && fits)
-    hipLaunchKernelGGL(agg_finalize_bf16<64>, fgrid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL(agg_finalize_bf16<64>, ggrid, dim3(256), 0, s, a);
   else if (dtype == 1)
     hipLaunchKernelGGL(agg_finalize<float>, fgrid, dim3(256), 0, s, a);
   else
