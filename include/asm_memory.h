@@ -35,6 +35,11 @@
  *     counted in elements must be a multiple of 8.
  *   - Outputs must not overlap inputs unless an entry point says so.
  *   - Two calls that share a workspace must not run concurrently.
+ *   - Two environment variables override the decode launch shape, for
+ *     tuning: ASM_DECODE_WAVES (waves of the MFMA-path grid) and
+ *     ASM_DECODE_SPLIT (local tokens per item on the VALU path, a multiple
+ *     of 32).  The decode workspace size depends on them, so they must not
+ *     change between asm_decode_step_ws and the calls it sizes.
  */
 #ifndef ASM_MEMORY_H
 #define ASM_MEMORY_H
