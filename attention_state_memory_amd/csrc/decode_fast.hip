@@ -401,11 +401,23 @@ decode_fast_main(DecodeArgs a) {
   // work-share arithmetic and the buffer resources in scalar registers
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
+  const int64_t gw = int64_t(blockIdx.x) * 4 + w;
+  const int64_t W = a.n_waves;
+  const int64_t SU = int64_t(a.Hq) * a.score_uph;
+
+  // The lengths of the first 256 sequences are loaded now and scanned after
+  // the scoring share, which does not need them.
+  const int v_first = (int(threadIdx.x) < a.B && seq_valid(a, threadIdx.x)) ? (a.kv_len[threadIdx.x] + 31) >> 5 : 0;
+
+  // scoring share first: every wave scores at the same time, so the table
+  // streams with the whole grid's memory parallelism
+  score_range<D>(a, int(share_lo(gw, SU, W)), int(share_lo(gw + 1, SU, W)), int(SU));
+
   // tiles per kv head of every sequence, exclusive prefix over sequences
   int carry = 0;
   for (int base = 0; base < a.B; base += 256) {
     const int b = base + threadIdx.x;
-    const int v = (b < a.B && seq_valid(a, b)) ? (a.kv_len[b] + 31) >> 5 : 0;
+    const int v = base == 0 ? v_first : (b < a.B && seq_valid(a, b)) ? (a.kv_len[b] + 31) >> 5 : 0;
     int x = v;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -424,15 +436,7 @@ decode_fast_main(DecodeArgs a) {
   __syncthreads();
   if (blockIdx.x == 0)
     for (int b = threadIdx.x; b <= a.B; b += 256) a.tile_prefix[b] = tp[b];
-
-  const int64_t gw = int64_t(blockIdx.x) * 4 + w;
-  const int64_t W = a.n_waves;
-  const int64_t SU = int64_t(a.Hq) * a.score_uph;
   const int64_t U = int64_t(__builtin_amdgcn_readfirstlane(tp[a.B])) * a.Hkv;
-
-  // scoring share first: every wave scores at the same time, so the table
-  // streams with the whole grid's memory parallelism
-  score_range<D>(a, int(share_lo(gw, SU, W)), int(share_lo(gw + 1, SU, W)), int(SU));
 
   // Attention shares go to the first min(W, U) waves only, so that every
   // share holds at least one tile and the pieces of a segment sit at
