@@ -406,6 +406,8 @@ int asm_decode_step_hier(int dtype, int B, int Hq, int Hkv, int d, int K, int S,
     return fail(ASM_ERR_SHAPE, "need 1 <= S <= min(K, %d) (S=%d, K=%d)", asmk::kHierMaxSupers, S, K);
   if (p < 1 || p > asmk::kHierMaxProbes)
     return fail(ASM_ERR_SHAPE, "need 1 <= p <= %d (p=%d)", asmk::kHierMaxProbes, p);
+  if (int64_t(K) * d * 2 >= (int64_t(1) << 31))
+    return fail(ASM_ERR_SHAPE, "one head's entry table must stay under 2 GiB (K=%d)", K);
   if (!SC || !scinv || !offsets || !members) return fail(ASM_ERR_NULL, "SC, scinv, offsets and members are required");
   ASM_TRY(check_bf16_ptrs(dtype, {SC}));
   asmk::HierArgs h{};
