@@ -577,10 +577,14 @@ int asm_kmeans_assign(int dtype, int H, int N, int K, int d, const void* X, cons
 }
 
 // ---------------------------------------------------------------------------
+static bool aggregate_lds_sort(int K) { return K <= asmk::kAggLdsMaxK; }
+
 static size_t aggregate_ws_bytes(int H, int N, int K) {
   size_t off = asmk::align_up(size_t(H) * (K + 1) * sizeof(int32_t), kAlign);
   off += asmk::align_up(size_t(H) * K * sizeof(int32_t), kAlign);
   off += asmk::align_up(size_t(H) * N * sizeof(int32_t), kAlign);
+  if (aggregate_lds_sort(K))
+    off += asmk::align_up(size_t(H) * K * asmk::agg_chunks(N) * sizeof(int32_t), kAlign);
   return off;
 }
 
@@ -617,6 +621,8 @@ int asm_aggregate(int dtype, int H, int N, int K, int d, const void* X, const in
   a.cursor = reinterpret_cast<int32_t*>(w + off);
   off += asmk::align_up(size_t(H) * K * sizeof(int32_t), kAlign);
   a.perm = reinterpret_cast<int32_t*>(w + off);
+  off += asmk::align_up(size_t(H) * N * sizeof(int32_t), kAlign);
+  a.part = aggregate_lds_sort(K) ? reinterpret_cast<int32_t*>(w + off) : nullptr;
   return hip_status(asmk::launch_aggregate(a, dtype, stream), "aggregate");
 }
 

@@ -149,7 +149,11 @@ struct AggregateArgs {
   int32_t* offsets;  // [H, K+1] workspace
   int32_t* cursor;   // [H, K]   workspace
   int32_t* perm;     // [H, N]   workspace
+  int32_t* part;     // [H, nchunks, K] workspace for the LDS counting sort, or NULL
 };
+constexpr int kAggChunk = 4096;      // queries per counting-sort workgroup
+constexpr int kAggLdsMaxK = 16384;   // largest K whose counters fit in LDS
+inline int agg_chunks(int N) { return (N + kAggChunk - 1) / kAggChunk; }
 hipError_t launch_aggregate(const AggregateArgs& a, int dtype, hipStream_t s);
 
 }  // namespace asmk

@@ -10,10 +10,13 @@
 // merges the members' states with the online-softmax rule), Eficiencia (a
 // long prefix is processed in chunks merged by the same identity).
 //
-// Aggregation is a counting sort of the queries by cluster followed by one
-// wave per cluster:
-//   fill(count) -> histogram(count) -> per-head exclusive scan (offsets,
-//   cursor) -> scatter (perm) -> finalize (mean, cinv, Z-weighted state).
+// Aggregation is a counting sort of the queries by cluster followed by the
+// per-cluster finalize (mean, cinv, Z-weighted state):
+//   K <= kAggLdsMaxK: per (head, chunk of queries) counts in LDS -> per-head
+//     scan of the (cluster, chunk) counts (count, offsets) -> scatter (perm)
+//     with LDS cursors;
+//   larger K: fill(count) -> histogram with global atomics -> per-head scan
+//     (offsets, cursor) -> scatter with global atomics.
 // Sums run in float64: a bf16 mean is then the float64 mean rounded once to
 // bf16, and the member order inside a cluster (set by atomics) does not
 // change the result unless a float64 sum is inexact.
@@ -70,6 +73,90 @@ __global__ void agg_histogram(AggregateArgs a) {
     const int h = int(t / a.N);
     const int k = a.idx[t];
     if (k >= 0 && k < a.K) atomicAdd(&a.count[size_t(h) * a.K + k], 1);
+  }
+}
+
+// ---- counting sort with the counters in LDS (K <= kAggLdsMaxK) ---------------
+// Workgroup (h, c) counts the members of every cluster among queries
+// [c*kAggChunk, (c+1)*kAggChunk) of head h in LDS and stores the counts as
+// part[h, c, k].  agg_scan_parts turns part into exclusive offsets (clusters
+// in order, chunks in order within a cluster) and writes count and offsets;
+// agg_scatter_lds then places every query at its cluster's next slot with
+// LDS atomics.  The order of the queries inside one (cluster, chunk) is
+// unspecified.
+__global__ void __launch_bounds__(256) agg_hist_lds(AggregateArgs a, int nch) {
+  extern __shared__ int32_t hs[];
+  const int h = blockIdx.x / nch, c = blockIdx.x % nch;
+  for (int k = threadIdx.x; k < a.K; k += 256) hs[k] = 0;
+  __syncthreads();
+  const int i0 = c * kAggChunk, i1 = min(a.N, i0 + kAggChunk);
+  const int32_t* idx = a.idx + size_t(h) * a.N;
+  for (int i = i0 + threadIdx.x; i < i1; i += 256) {
+    const int k = idx[i];
+    if (k >= 0 && k < a.K) atomicAdd(&hs[k], 1);
+  }
+  __syncthreads();
+  int32_t* part = a.part + (size_t(h) * nch + c) * a.K;
+  for (int k = threadIdx.x; k < a.K; k += 256) part[k] = hs[k];
+}
+
+// One 1024-thread workgroup per head; thread t of a pass owns cluster
+// base + t and its nch chunk counts.
+__global__ void __launch_bounds__(1024) agg_scan_parts(AggregateArgs a, int nch) {
+  __shared__ int32_t wsum[16];
+  __shared__ int32_t carry_s;
+  const int h = blockIdx.x;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  int32_t* part = a.part + size_t(h) * a.K * nch;
+  int32_t* off = a.offsets + size_t(h) * (a.K + 1);
+  int32_t* cnt = a.count + size_t(h) * a.K;
+  if (t == 0) carry_s = 0;
+  __syncthreads();
+  for (int base = 0; base < a.K; base += 1024) {
+    const int k = base + t;
+    int32_t v = 0;
+    if (k < a.K)
+      for (int c = 0; c < nch; ++c) v += part[size_t(c) * a.K + k];
+    int32_t x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int32_t y = __shfl_up(x, o, 64);
+      if (lane >= o) x += y;
+    }
+    if (lane == 63) wsum[w] = x;
+    __syncthreads();
+    int32_t before = carry_s;
+    for (int ww = 0; ww < w; ++ww) before += wsum[ww];
+    const int32_t excl = before + x - v;
+    if (k < a.K) {
+      off[k] = excl;
+      cnt[k] = v;
+      int32_t run = excl;
+      for (int c = 0; c < nch; ++c) {
+        const int32_t n = part[size_t(c) * a.K + k];
+        part[size_t(c) * a.K + k] = run;
+        run += n;
+      }
+    }
+    __syncthreads();
+    if (t == 1023) carry_s = excl + v;
+    __syncthreads();
+  }
+  if (t == 0) off[a.K] = carry_s;
+}
+
+__global__ void __launch_bounds__(256) agg_scatter_lds(AggregateArgs a, int nch) {
+  extern __shared__ int32_t cur[];
+  const int h = blockIdx.x / nch, c = blockIdx.x % nch;
+  const int32_t* part = a.part + (size_t(h) * nch + c) * a.K;
+  for (int k = threadIdx.x; k < a.K; k += 256) cur[k] = part[k];
+  __syncthreads();
+  const int i0 = c * kAggChunk, i1 = min(a.N, i0 + kAggChunk);
+  const int32_t* idx = a.idx + size_t(h) * a.N;
+  int32_t* perm = a.perm + size_t(h) * a.N;
+  for (int i = i0 + threadIdx.x; i < i1; i += 256) {
+    const int k = idx[i];
+    if (k >= 0 && k < a.K) perm[atomicAdd(&cur[k], 1)] = i;
   }
 }
 
@@ -353,10 +440,19 @@ hipError_t launch_aggregate(const AggregateArgs& a, int dtype, hipStream_t s) {
   const int64_t HK = int64_t(a.H) * a.K, HN = int64_t(a.H) * a.N;
   if (HK == 0) return hipSuccess;
   auto grid_for = [](int64_t n) { return dim3(unsigned((n + 255) / 256 < 65536 ? (n + 255) / 256 : 65536)); };
-  hipLaunchKernelGGL(fill_i32, grid_for(HK), dim3(256), 0, s, a.count, HK, 0);
-  if (HN > 0) hipLaunchKernelGGL(agg_histogram, grid_for(HN), dim3(256), 0, s, a);
-  hipLaunchKernelGGL(agg_scan, dim3(a.H), dim3(1024), 0, s, a);
-  if (HN > 0) hipLaunchKernelGGL(agg_scatter, grid_for(HN), dim3(256), 0, s, a);
+  if (a.part != nullptr && a.K <= kAggLdsMaxK && a.N > 0) {
+    const int nch = agg_chunks(a.N);
+    const dim3 cgrid(unsigned(int64_t(a.H) * nch));
+    const size_t lds = size_t(a.K) * sizeof(int32_t);
+    hipLaunchKernelGGL(agg_hist_lds, cgrid, dim3(256), lds, s, a, nch);
+    hipLaunchKernelGGL(agg_scan_parts, dim3(a.H), dim3(1024), 0, s, a, nch);
+    hipLaunchKernelGGL(agg_scatter_lds, cgrid, dim3(256), lds, s, a, nch);
+  } else {
+    hipLaunchKernelGGL(fill_i32, grid_for(HK), dim3(256), 0, s, a.count, HK, 0);
+    if (HN > 0) hipLaunchKernelGGL(agg_histogram, grid_for(HN), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(agg_scan, dim3(a.H), dim3(1024), 0, s, a);
+    if (HN > 0) hipLaunchKernelGGL(agg_scatter, grid_for(HN), dim3(256), 0, s, a);
+  }
   const dim3 fgrid(unsigned((HK + 3) / 4));
   const bool fits = int64_t(a.N) * a.d * 4 < (int64_t(1) << 31);
   // the bf16 kernel serves 64*8/d clusters per wave, four waves per block
