@@ -79,8 +79,9 @@ __global__ void agg_histogram(AggregateArgs a) {
 // ---- counting sort with the counters in LDS (K <= kAggLdsMaxK) ---------------
 // Workgroup (h, c) counts the members of every cluster among queries
 // [c*kAggChunk, (c+1)*kAggChunk) of head h in LDS and stores the counts as
-// part[h, c, k].  agg_scan_parts turns part into exclusive offsets (clusters
-// in order, chunks in order within a cluster) and writes count and offsets;
+// part[h, c, k].  agg_scan_pass1/2 turn part into exclusive offsets
+// (clusters in order, chunks in order within a cluster) and write count and
+// offsets;
 // agg_scatter_lds then places every query at its cluster's next slot with
 // LDS atomics.  The order of the queries inside one (cluster, chunk) is
 // unspecified.
@@ -100,49 +101,74 @@ __global__ void __launch_bounds__(256) agg_hist_lds(AggregateArgs a, int nch) {
   for (int k = threadIdx.x; k < a.K; k += 256) part[k] = hs[k];
 }
 
-// One 1024-thread workgroup per head; thread t of a pass owns cluster
-// base + t and its nch chunk counts.
-__global__ void __launch_bounds__(1024) agg_scan_parts(AggregateArgs a, int nch) {
-  __shared__ int32_t wsum[16];
-  __shared__ int32_t carry_s;
-  const int h = blockIdx.x;
+// The scan of the (cluster, chunk) counts in two passes over blocks of 1024
+// clusters, one workgroup per (head, block); thread t owns cluster
+// 1024*blk + t.  Pass 1 writes each cluster's count, its offset within the
+// block and the block's total (kept in `cursor`, unused by this sort).
+__device__ __forceinline__ int32_t block_excl_scan_1024(int32_t v, int32_t* wsum, int32_t& total) {
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  int32_t* part = a.part + size_t(h) * a.K * nch;
-  int32_t* off = a.offsets + size_t(h) * (a.K + 1);
-  int32_t* cnt = a.count + size_t(h) * a.K;
-  if (t == 0) carry_s = 0;
-  __syncthreads();
-  for (int base = 0; base < a.K; base += 1024) {
-    const int k = base + t;
-    int32_t v = 0;
-    if (k < a.K)
-      for (int c = 0; c < nch; ++c) v += part[size_t(c) * a.K + k];
-    int32_t x = v;
+  int32_t x = v;
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int32_t y = __shfl_up(x, o, 64);
-      if (lane >= o) x += y;
-    }
-    if (lane == 63) wsum[w] = x;
-    __syncthreads();
-    int32_t before = carry_s;
-    for (int ww = 0; ww < w; ++ww) before += wsum[ww];
-    const int32_t excl = before + x - v;
-    if (k < a.K) {
-      off[k] = excl;
-      cnt[k] = v;
-      int32_t run = excl;
-      for (int c = 0; c < nch; ++c) {
-        const int32_t n = part[size_t(c) * a.K + k];
-        part[size_t(c) * a.K + k] = run;
-        run += n;
-      }
-    }
-    __syncthreads();
-    if (t == 1023) carry_s = excl + v;
-    __syncthreads();
+  for (int o = 1; o < 64; o <<= 1) {
+    const int32_t y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
   }
-  if (t == 0) off[a.K] = carry_s;
+  if (lane == 63) wsum[w] = x;
+  __syncthreads();
+  int32_t before = 0;
+  total = 0;
+  for (int ww = 0; ww < 16; ++ww) {
+    if (ww < w) before += wsum[ww];
+    total += wsum[ww];
+  }
+  return before + x - v;
+}
+
+__global__ void __launch_bounds__(1024) agg_scan_pass1(AggregateArgs a, int nch, int nkb) {
+  __shared__ int32_t wsum[16];
+  const int h = blockIdx.x / nkb, blk = blockIdx.x % nkb;
+  const int k = blk * 1024 + threadIdx.x;
+  const int32_t* part = a.part + size_t(h) * nch * a.K;
+  int32_t v = 0;
+  if (k < a.K)
+    for (int c = 0; c < nch; ++c) v += part[size_t(c) * a.K + k];
+  int32_t total;
+  const int32_t excl = block_excl_scan_1024(v, wsum, total);
+  if (k < a.K) {
+    a.count[size_t(h) * a.K + k] = v;
+    a.offsets[size_t(h) * (a.K + 1) + k] = excl;
+  }
+  if (threadIdx.x == 0) a.cursor[size_t(h) * nkb + blk] = total;
+}
+
+// Pass 2 adds the totals of the preceding blocks and turns the chunk counts
+// into the chunks' first slots.
+__global__ void __launch_bounds__(1024) agg_scan_pass2(AggregateArgs a, int nch, int nkb) {
+  __shared__ int32_t carry_s, total_s;
+  const int h = blockIdx.x / nkb, blk = blockIdx.x % nkb;
+  if (threadIdx.x == 0) {
+    int32_t c = 0, t = 0;
+    for (int b = 0; b < nkb; ++b) {
+      const int32_t s = a.cursor[size_t(h) * nkb + b];
+      if (b < blk) c += s;
+      t += s;
+    }
+    carry_s = c;
+    total_s = t;
+  }
+  __syncthreads();
+  const int k = blk * 1024 + threadIdx.x;
+  int32_t* part = a.part + size_t(h) * nch * a.K;
+  if (k < a.K) {
+    int32_t run = carry_s + a.offsets[size_t(h) * (a.K + 1) + k];
+    a.offsets[size_t(h) * (a.K + 1) + k] = run;
+    for (int c = 0; c < nch; ++c) {
+      const int32_t n = part[size_t(c) * a.K + k];
+      part[size_t(c) * a.K + k] = run;
+      run += n;
+    }
+  }
+  if (blk == nkb - 1 && threadIdx.x == 0) a.offsets[size_t(h) * (a.K + 1) + a.K] = total_s;
 }
 
 __global__ void __launch_bounds__(256) agg_scatter_lds(AggregateArgs a, int nch) {
@@ -444,8 +470,10 @@ hipError_t launch_aggregate(const AggregateArgs& a, int dtype, hipStream_t s) {
     const int nch = agg_chunks(a.N);
     const dim3 cgrid(unsigned(int64_t(a.H) * nch));
     const size_t lds = size_t(a.K) * sizeof(int32_t);
+    const int nkb = (a.K + 1023) / 1024;
     hipLaunchKernelGGL(agg_hist_lds, cgrid, dim3(256), lds, s, a, nch);
-    hipLaunchKernelGGL(agg_scan_parts, dim3(a.H), dim3(1024), 0, s, a, nch);
+    hipLaunchKernelGGL(agg_scan_pass1, dim3(unsigned(a.H * nkb)), dim3(1024), 0, s, a, nch, nkb);
+    hipLaunchKernelGGL(agg_scan_pass2, dim3(unsigned(a.H * nkb)), dim3(1024), 0, s, a, nch, nkb);
     hipLaunchKernelGGL(agg_scatter_lds, cgrid, dim3(256), lds, s, a, nch);
   } else {
     hipLaunchKernelGGL(fill_i32, grid_for(HK), dim3(256), 0, s, a.count, HK, 0);
