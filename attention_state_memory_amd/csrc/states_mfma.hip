@@ -17,13 +17,19 @@
 //   O^T += V^T P^T   (16x16x32 f16 MFMA; A = V^T, gathered from the
 //                     row-major fp16 V tile in LDS by transposing reads
 //                     (ds_read_b64_tr_b16), B = the probabilities, already
-//                     in the B-operand layout).
-// The probability-value products run in fp16: P <= 1 and fp16 keeps 3 more
-// mantissa bits than bf16; V is converted to fp16 once per call into the
-// workspace, so its values must stay below 65504.  At each chunk
-// boundary the chunk state (O/l, m + log l) is written (if requested) and
-// merged into the running state, which lives in the output (A, LSE) between
-// chunks: every wave reads back only rows it wrote itself.
+//                     in the B-operand layout);
+//   l += 1^T P^T     (the same MFMA with an all-ones A operand), so the
+//                     softmax denominator is the sum of exactly the fp16
+//                     probabilities that enter O, summed on the matrix
+//                     cores instead of the vector ALUs.
+// The softmax runs once per 64-key tile (one maximum, reduced across the
+// wave's four 16-lane groups with the gfx950 lane-swap instructions).  The
+// probability-value products run in fp16: P < 2^8 (lazy maximum, below) and
+// fp16 keeps 3 more mantissa bits than bf16; V is converted to fp16 once per
+// call into the workspace, so its values must stay below 65504.  At each
+// chunk boundary the chunk state (O/l, m + log l) is written (if requested)
+// and merged into the running state, which lives in the output (A, LSE)
+// between chunks: every wave reads back only rows it wrote itself.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -130,44 +136,55 @@ __global__ void v_to_f16_kernel(const u32x4* src, u32x4* dst, int64_t n8) {
 
 }  // namespace
 
-// Online softmax of one 32-key block for query column tile qt: scores
-// st[kk][qt][i] belong to key 32*ks + 16*kk + 4*grp + i.  The reference
-// maximum m is lazy: it only moves when the block's maximum exceeds it by
-// more than kLazy (base-2 units), so most blocks rescale nothing; the
+// Maximum over the four 16-lane groups of a wave (lanes j, j+16, j+32, j+48),
+// with the two lane-swap instructions of gfx950 instead of LDS permutes.
+__device__ __forceinline__ float group4_max(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const float y = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  const unsigned v = __float_as_uint(y);
+  const auto t = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
+}
+
+// Online softmax of one 64-key tile for query column tile qt: scores
+// st[ks][kk][qt][i] belong to key 32*ks + 16*kk + 4*grp + i.  The reference
+// maximum m is lazy: it only moves when the tile's maximum exceeds it by more
+// than kLazy (base-2 units), so most tiles rescale nothing; the
 // probabilities then stay below 2^kLazy, far inside fp16.  Exponents are
 // exp2(s * scale2 - m) with one rounding (scale2 > 0).  Returns whether m
 // moved (then O must be scaled by alpha[qt]).
 constexpr float kLazy = 8.0f;
 
 template <bool kFull>
-__device__ __forceinline__ bool softmax_block(const f32x4 (&st)[2][2], int qt, int ks, int grp,
-                                              int nvalid, float scale2, float (&m)[2],
-                                              float (&l)[2], float (&alpha)[2], f16x8 (&pb)[2]) {
+__device__ __forceinline__ bool softmax_tile(const f32x4 (&st)[2][2][2], int qt, int grp,
+                                             int nvalid, float scale2, float (&m)[2],
+                                             float (&alpha)[2], f16x8 (&pb)[2][2]) {
   float mt = -INFINITY;
 #pragma unroll
-  for (int kk = 0; kk < 2; ++kk)
+  for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bool ok = kFull || 32 * ks + 16 * kk + 4 * grp + i < nvalid;
-      mt = fmaxf(mt, ok ? st[kk][qt][i] : -INFINITY);
-    }
-  mt = fmaxf(mt, shfl_xor_f(mt, 16));
-  mt = fmaxf(mt, shfl_xor_f(mt, 32));
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool ok = kFull || 32 * ks + 16 * kk + 4 * grp + i < nvalid;
+        mt = fmaxf(mt, ok ? st[ks][kk][qt][i] : -INFINITY);
+      }
+  mt = group4_max(mt);
   const float mts = mt * scale2;
-  const bool up = mts > m[qt] + kLazy;  // always true for the first block
+  const bool up = mts > m[qt] + kLazy;  // always true for the first tile
   const float mn = up ? mts : m[qt];
   alpha[qt] = up ? __builtin_amdgcn_exp2f(m[qt] - mn) : 1.0f;
-  float lp = 0.0f;
 #pragma unroll
-  for (int kk = 0; kk < 2; ++kk)
+  for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bool ok = kFull || 32 * ks + 16 * kk + 4 * grp + i < nvalid;
-      const float p = ok ? __builtin_amdgcn_exp2f(fmaf(st[kk][qt][i], scale2, -mn)) : 0.0f;
-      lp += p;
-      pb[qt][4 * kk + i] = (_Float16)p;
-    }
-  l[qt] = l[qt] * alpha[qt] + lp;
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool ok = kFull || 32 * ks + 16 * kk + 4 * grp + i < nvalid;
+        const float p = ok ? __builtin_amdgcn_exp2f(fmaf(st[ks][kk][qt][i], scale2, -mn)) : 0.0f;
+        pb[ks][qt][4 * kk + i] = (_Float16)p;
+      }
   m[qt] = mn;
   return up;
 }
@@ -206,7 +223,9 @@ states_mfma_kernel(StatesArgs a, int row_blocks, int hsubs) {
   const bool acc_in = a.accumulate != 0;
 
   float O[DT][2][4];
-  float m[2], l[2];
+  f32x4 lacc[2];  // per query column: sum of the (fp16) probabilities, in every row
+  float m[2];
+  const f16x8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
   Staged<D> stg;
   int buf_i = 0;
   bool have_tile = false;
@@ -216,7 +235,7 @@ states_mfma_kernel(StatesArgs a, int row_blocks, int hsubs) {
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
       m[qt] = -INFINITY;
-      l[qt] = 0.0f;
+      lacc[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -237,10 +256,11 @@ states_mfma_kernel(StatesArgs a, int row_blocks, int hsubs) {
       const int nk = k0 + kKeys < c_hi ? k0 + kKeys : c_hi;
       stage_load<D>(stg, rk, rv, nk);
       const int nvalid = min(kKeys, c_hi - k0);
+      // scores of the whole tile: st[ks][kk][qt] for keys 32*ks + 16*kk + 4*grp + i
+      // and query column r16 of tile qt
+      f32x4 st[2][2][2];
 #pragma unroll
-      for (int ks = 0; ks < kKeys / 32; ++ks) {
-        // scores of keys 32*ks + 16*kk + 4*grp + i (kk = 0, 1) for query column r16
-        f32x4 st[2][2];
+      for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
           bf16x8 ka[KS];
@@ -250,52 +270,61 @@ states_mfma_kernel(StatesArgs a, int row_blocks, int hsubs) {
                 cur + (32 * ks + 16 * kk + r16) * S::kKRow + (32 * s + 8 * grp) * 2));
 #pragma unroll
           for (int qt = 0; qt < 2; ++qt) {
-            st[kk][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            st[ks][kk][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s = 0; s < KS; ++s)
-              st[kk][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[s], qb[qt][s], st[kk][qt], 0, 0, 0);
+              st[ks][kk][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[s], qb[qt][s], st[ks][kk][qt], 0, 0, 0);
           }
         }
-        f16x8 pb[2];
-        float alpha[2];
-        const bool up0 = nvalid >= kKeys
-                             ? softmax_block<true>(st, 0, ks, grp, nvalid, a.scale2, m, l, alpha, pb)
-                             : softmax_block<false>(st, 0, ks, grp, nvalid, a.scale2, m, l, alpha, pb);
-        const bool up1 = nvalid >= kKeys
-                             ? softmax_block<true>(st, 1, ks, grp, nvalid, a.scale2, m, l, alpha, pb)
-                             : softmax_block<false>(st, 1, ks, grp, nvalid, a.scale2, m, l, alpha, pb);
-        if (__any(up0 || up1)) {
+      f16x8 pb[2][2];
+      float alpha[2];
+      const bool up0 = nvalid >= kKeys
+                           ? softmax_tile<true>(st, 0, grp, nvalid, a.scale2, m, alpha, pb)
+                           : softmax_tile<false>(st, 0, grp, nvalid, a.scale2, m, alpha, pb);
+      const bool up1 = nvalid >= kKeys
+                           ? softmax_tile<true>(st, 1, grp, nvalid, a.scale2, m, alpha, pb)
+                           : softmax_tile<false>(st, 1, grp, nvalid, a.scale2, m, alpha, pb);
+      if (__any(up0 || up1)) {
 #pragma unroll
-          for (int dt = 0; dt < DT; ++dt)
+        for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-            for (int qt = 0; qt < 2; ++qt)
+          for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
-              for (int i = 0; i < 4; ++i) O[dt][qt][i] *= alpha[qt];
-        }
-        // O^T += V^T P^T over these 32 keys; the k index of lane group grp is
-        // keys {4grp..4grp+3} then {16+4grp..16+4grp+3}, matching pb
-        const char* vbase = cur + S::kKBytes;
+            for (int i = 0; i < 4; ++i) O[dt][qt][i] *= alpha[qt];
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) lacc[qt][i] *= alpha[qt];
+      }
+      // O^T += V^T P^T over the tile's 64 keys; the k index of lane group grp
+      // in half ks is keys 32*ks + {4grp..4grp+3} then 32*ks + 16 + {4grp..4grp+3},
+      // matching pb[ks]
+      const char* vbase = cur + S::kKBytes;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
           const f16x8 va = load_vt<D>(vbase, dt, 32 * ks + 4 * grp, 32 * ks + 16 + 4 * grp, r16);
 #pragma unroll
           for (int qt = 0; qt < 2; ++qt) {
             f32x4 o = {O[dt][qt][0], O[dt][qt][1], O[dt][qt][2], O[dt][qt][3]};
-            o = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb[qt], o, 0, 0, 0);
+            o = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb[ks][qt], o, 0, 0, 0);
 #pragma unroll
             for (int i = 0; i < 4; ++i) O[dt][qt][i] = o[i];
           }
         }
-      }
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt)
+          lacc[qt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pb[ks][qt], lacc[qt], 0, 0, 0);
       stage_store<D>(smem + (buf_i ^ 1) * S::kBuf, stg);
       buf_i ^= 1;
     }
     // chunk state and running merge (per query column r16 of each qt)
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
-      float lt = l[qt];
-      lt += shfl_xor_f(lt, 16);
-      lt += shfl_xor_f(lt, 32);
+      const float lt = lacc[qt][0];
       const bool empty = m[qt] == -INFINITY;
       const float inv = empty ? 0.0f : 1.0f / lt;
       const float lse_c = empty ? -INFINITY : (m[qt] + __log2f(lt)) * ASM_LN2;
