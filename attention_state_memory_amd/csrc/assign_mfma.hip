@@ -9,7 +9,9 @@
 // GEMM X C^T with a row argmax fused into its epilogue, so the N x K score
 // matrix never leaves registers.  One workgroup owns 256 query rows (64 per
 // wave, held in registers as MFMA A operands) and streams the head's whole
-// centroid table through LDS in double-buffered tiles of 128 centroids.  Each
+// centroid table through LDS in double-buffered tiles of 64 centroids.  The
+// small tiles (35 KB of LDS) and a 168-register budget let three waves share
+// each SIMD, so one wave's argmax epilogue overlaps another's MFMAs.  Each
 // lane keeps, for each of its 16 rows, the best score seen in its column
 // slot; a DPP reduction over the 16 lanes of a row finishes the argmax.
 // Workgroups are mapped XCD-aware: each XCD walks a contiguous range of
@@ -23,7 +25,7 @@ namespace {
 
 constexpr int kRowsPerWave = 64;              // 4 MFMA row tiles of 16
 constexpr int kRowsPerWG = 4 * kRowsPerWave;  // 256
-constexpr int kTileCols = 128;                // centroids per LDS tile
+constexpr int kTileCols = 64;                 // centroids per LDS tile
 constexpr int kXcds = 8;
 
 template <int D>
@@ -69,7 +71,8 @@ __device__ __forceinline__ void commit_tile(char* buf, const u32x4 (&reg)[kTileC
 }  // namespace
 
 template <int D>
-__global__ void __launch_bounds__(256) assign_mfma_kernel(AssignArgs a, int row_blocks, int per_xcd) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3)))
+assign_mfma_kernel(AssignArgs a, int row_blocks, int per_xcd) {
   constexpr int KS = D / 32;
   constexpr int kPer = kTileCols * (D / 8) / 256;
   __shared__ __attribute__((aligned(16))) char smem[AssignSmem<D>::kBytes];
@@ -117,7 +120,7 @@ __global__ void __launch_bounds__(256) assign_mfma_kernel(AssignArgs a, int row_
     if (kt + 1 < ntiles) stage_tile<D>(nxt, rc, ri, (kt + 1) * kTileCols, reg, ci);
     const float* cil = reinterpret_cast<const float*>(cur + AssignSmem<D>::kTileBytes);
     const bool partial = (kt + 1) * kTileCols > a.K;
-#pragma unroll 2
+#pragma unroll 1  // unrolling raises the register count past three waves per SIMD
     for (int ct = 0; ct < kTileCols / 16; ++ct) {
       // B operand: centroid column ct*16 + r16, d chunk 32*s + 8*grp
       bf16x8 cb[KS];
