@@ -122,3 +122,45 @@ def test_binding_refuses_host_tensors():
     import torch
     with pytest.raises(TypeError):
         api.centroid_inv_norms(torch.zeros(1, 2, 8))
+
+
+C_PROGRAM = r"""
+#include <stdio.h>
+#include <string.h>
+#include "asm_memory.h"
+
+int main(void) {
+  /* every entry point has a C prototype; taking its address makes the
+     linker resolve it against the shared library */
+  const void* fns[] = {%s};
+  size_t n = sizeof fns / sizeof fns[0];
+  for (size_t i = 0; i < n; ++i)
+    if (fns[i] == NULL) return 2;
+  if (asm_abi_version() != ASM_ABI_VERSION) return 3;
+  if (strcmp(asm_status_str(ASM_OK), "ok") != 0) return 4;
+  printf("%%d entry points\n", (int)n);
+  return 0;
+}
+"""
+
+
+def test_header_compiles_and_links_as_c(tmp_path):
+    """include/asm_memory.h is plain C: a C11 program that names every entry
+    point compiles without warnings, links against the library and calls
+    its host-only functions."""
+    gcc = subprocess.run(["which", "gcc"], capture_output=True, text=True).stdout.strip()
+    if not gcc:
+        pytest.skip("no C compiler")
+    names = declared_functions()
+    src = tmp_path / "abi_c.c"
+    src.write_text(C_PROGRAM % ", ".join(f"(const void*)&{n}" for n in names))
+    exe = tmp_path / "abi_c"
+    libdir = os.path.dirname(api.LIB_PATH)
+    cmd = [gcc, "-std=c11", "-Wall", "-Wextra", "-Werror", "-Wno-pedantic", "-D__HIP_PLATFORM_AMD__",
+           "-I" + os.path.join(ROOT, "include"), "-I/opt/rocm/include", str(src), "-o", str(exe),
+           "-L" + libdir, "-l:" + os.path.basename(api.LIB_PATH), "-Wl,-rpath," + libdir]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert r.returncode == 0, (r.returncode, r.stdout, r.stderr)
+    assert r.stdout.strip() == f"{len(names)} entry points"
