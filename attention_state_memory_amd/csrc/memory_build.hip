@@ -334,8 +334,10 @@ __global__ void __launch_bounds__(256) agg_finalize(AggregateArgs a) {
 // clusters at once.  Lane `sub` of a group owns dims 8*sub .. 8*sub+7 of
 // the cluster: it sums them over all members in float64 (eight member rows
 // in flight), rounds the mean once, and for the states weighs the members'
-// a rows (two 16-byte pieces per lane) by Z.
-template <int D>
+// a rows (two 16-byte pieces per lane) by Z.  The mean step without states
+// is its own instantiation (kStates = false): it needs 70 registers instead
+// of 106, so more waves per SIMD overlap the dependent rounds.
+template <int D, bool kStates>
 __global__ void __launch_bounds__(256) agg_finalize_bf16(AggregateArgs a) {
   constexpr int LG = D / 8;   // lanes per cluster
   constexpr int NG = 64 / LG;  // clusters per wave
@@ -404,7 +406,7 @@ __global__ void __launch_bounds__(256) agg_finalize_bf16(AggregateArgs a) {
   for (int m = 1; m < LG; m <<= 1) ss += __shfl_xor(ss, m, 64);
   if (live && sub == 0) a.cinv[it] = ss > 0.0 ? float(1.0 / sqrt(ss)) : 0.0f;
 
-  if (a.Abar == nullptr || !live) return;
+  if (!kStates || !live) return;
   // ---- state: Z-weighted mean of the members' a, mean of their Z
   float* ab = a.Abar + size_t(it) * D + 8 * sub;
   const float* LSE = a.LSE + size_t(h) * a.N;
@@ -486,14 +488,18 @@ hipError_t launch_aggregate(const AggregateArgs& a, int dtype, hipStream_t s) {
   // the bf16 kernel serves 64*8/d clusters per wave, four waves per block
   const int64_t cpb = int64_t(4) * (64 * 8 / (a.d > 0 ? a.d : 1));
   const dim3 ggrid(unsigned((HK + cpb - 1) / cpb));
-  if (dtype == 0 && a.d == 128 && fits)
-    hipLaunchKernelGGL(agg_finalize_bf16<128>, ggrid, dim3(256), 0, s, a);
-  else if (dtype == 0 && a.d == 64 && fits)
-    hipLaunchKernelGGL(agg_finalize_bf16<64>, ggrid, dim3(256), 0, s, a);
-  else if (dtype == 1)
+  const bool states = a.Abar != nullptr;
+  if (dtype == 0 && a.d == 128 && fits) {
+    if (states) hipLaunchKernelGGL((agg_finalize_bf16<128, true>), ggrid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((agg_finalize_bf16<128, false>), ggrid, dim3(256), 0, s, a);
+  } else if (dtype == 0 && a.d == 64 && fits) {
+    if (states) hipLaunchKernelGGL((agg_finalize_bf16<64, true>), ggrid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((agg_finalize_bf16<64, false>), ggrid, dim3(256), 0, s, a);
+  } else if (dtype == 1) {
     hipLaunchKernelGGL(agg_finalize<float>, fgrid, dim3(256), 0, s, a);
-  else
+  } else {
     hipLaunchKernelGGL(agg_finalize<uint16_t>, fgrid, dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 
