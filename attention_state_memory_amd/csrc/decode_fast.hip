@@ -21,6 +21,8 @@
 // writes one partial state per (sequence, kv head) segment it touches.  decode_fast_combine (one wave per (b, h))
 // reduces the keys to the index, gathers the memory state and merges it
 // with the segment's partial states.
+#include <atomic>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -585,10 +587,13 @@ static int occupancy_waves() {
 }
 
 int decode_fast_waves_per_cu(int d, int G) {
-  static int cache[2][4] = {{0}};
+  // Computed once per (d, G); host threads may race to fill an entry, but
+  // they store the same value and the accesses are atomic.
+  static std::atomic<int> cache[2][4];
   const int di = d == 128 ? 0 : 1;
   const int gi = G == 1 ? 0 : G == 2 ? 1 : G == 4 ? 2 : 3;
-  if (cache[di][gi] == 0) {
+  int cached = cache[di][gi].load(std::memory_order_relaxed);
+  if (cached == 0) {
     int v = 4;
     if (d == 128) {
       v = G == 1 ? occupancy_waves<128, 1>() : G == 2 ? occupancy_waves<128, 2>()
@@ -597,9 +602,10 @@ int decode_fast_waves_per_cu(int d, int G) {
       v = G == 1 ? occupancy_waves<64, 1>() : G == 2 ? occupancy_waves<64, 2>()
         : G == 4 ? occupancy_waves<64, 4>() : occupancy_waves<64, 8>();
     }
-    cache[di][gi] = v;
+    cache[di][gi].store(v, std::memory_order_relaxed);
+    cached = v;
   }
-  return cache[di][gi];
+  return cached;
 }
 
 hipError_t launch_decode_fast(const DecodeArgs& a, hipStream_t s) {
