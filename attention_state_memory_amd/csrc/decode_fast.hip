@@ -413,7 +413,16 @@ decode_fast_main(DecodeArgs a) {
 
   // scoring share first: every wave scores at the same time, so the table
   // streams with the whole grid's memory parallelism
-  score_range<D>(a, int(share_lo(gw, SU, W)), int(share_lo(gw + 1, SU, W)), int(SU));
+  // When the grid has a wave for every unit (small steps, which are latency-
+  // bound), the scoring units go to the last SU waves and the attention tiles
+  // to the first ones, so that no wave does both one after the other.
+  const int64_t Umax = int64_t(a.B) * a.Hkv * ((int64_t(a.max_kv_len) + 31) / 32);
+  if (SU + Umax <= W) {
+    const int64_t su = gw - (W - SU);
+    if (su >= 0) score_range<D>(a, int(su), int(su + 1), int(SU));
+  } else {
+    score_range<D>(a, int(share_lo(gw, SU, W)), int(share_lo(gw + 1, SU, W)), int(SU));
+  }
 
   // tiles per kv head of every sequence, exclusive prefix over sequences
   int carry = 0;
