@@ -236,8 +236,9 @@ int decode_impl(int dtype, int B, int Hq, int Hkv, int d, int K, float scale,
       hier->q = a.q;
       hier->keys = a.keys;
       hier->probes_out = probes_base ? probes_base + size_t(b0) * Hq * hier->p : nullptr;
-      const int sth = hip_status(asmk::launch_hier_lookup(*hier, stream), "decode_step_hier");
+      const int sth = hip_status(asmk::launch_decode_hier(a, *hier, stream), "decode_step_hier");
       if (sth != ASM_OK) return sth;
+      continue;
     }
     const int st = hip_status(asmk::launch_decode(a, dtype, stream), "decode_step");
     if (st != ASM_OK) return st;

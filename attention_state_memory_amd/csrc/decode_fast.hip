@@ -24,6 +24,7 @@
 #include <atomic>
 
 #include "common.hpp"
+#include "hier_lookup.hpp"
 #include "kernels.hpp"
 
 namespace asmk {
@@ -393,9 +394,9 @@ __device__ __forceinline__ void attn_piece(const DecodeArgs& a, int b, int g, in
 }  // namespace
 
 // ---------------------------------------------------------------------------
+// One workgroup (block index blk) of the main grid.
 template <int D, int G, bool kPrefetch>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kPrefetch ? 2 : 3)))
-decode_fast_main(DecodeArgs a) {
+__device__ __forceinline__ void main_block(const DecodeArgs& a, int blk) {
   __shared__ int32_t tp[kFastMaxBatch + 1];
   __shared__ int32_t wsum[4];
   __shared__ float pls[4 * 32 * G];
@@ -403,7 +404,7 @@ decode_fast_main(DecodeArgs a) {
   // work-share arithmetic and the buffer resources in scalar registers
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
-  const int64_t gw = int64_t(blockIdx.x) * 4 + w;
+  const int64_t gw = int64_t(blk) * 4 + w;
   const int64_t W = a.n_waves;
   const int64_t SU = int64_t(a.Hq) * a.score_uph;
 
@@ -445,7 +446,7 @@ decode_fast_main(DecodeArgs a) {
   }
   if (threadIdx.x == 0) tp[a.B] = carry;
   __syncthreads();
-  if (blockIdx.x == 0)
+  if (blk == 0)
     for (int b = threadIdx.x; b <= a.B; b += 256) a.tile_prefix[b] = tp[b];
   const int64_t U = int64_t(__builtin_amdgcn_readfirstlane(tp[a.B])) * a.Hkv;
 
@@ -474,6 +475,27 @@ decode_fast_main(DecodeArgs a) {
     attn_piece<D, G, kPrefetch>(a, b, g, j0, j0 + cnt, gw + int64_t(b) * a.Hkv + g, pl);
     t += cnt;
   }
+}
+
+template <int D, int G, bool kPrefetch>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kPrefetch ? 2 : 3)))
+decode_fast_main(DecodeArgs a) {
+  main_block<D, G, kPrefetch>(a, int(blockIdx.x));
+}
+
+// The two-level lookup fused into the main grid: the first lookup_blocks
+// workgroups run the lookup (one per sequence, head and probe rank) and the
+// rest run the attention shares (scoring off).  The two roles share no
+// data inside the kernel -- the lookup writes the unit keys that the combine
+// reduces -- so at small batch they run side by side instead of one launch
+// after the other.
+template <int D, int G, bool kPrefetch>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kPrefetch ? 2 : 3)))
+decode_fast_main_hier(DecodeArgs a, HierArgs h, int lookup_blocks) {
+  if (int(blockIdx.x) < lookup_blocks)
+    hier_lookup_block<D>(h, int(blockIdx.x));
+  else
+    main_block<D, G, kPrefetch>(a, int(blockIdx.x) - lookup_blocks);
 }
 
 // One wave per (b, h): index from the unit keys, gather of the memory
@@ -581,6 +603,14 @@ bool decode_fast_path(int dtype, int d, int G, int64_t kv_tok_stride, int max_kv
 }
 
 template <int D, int G>
+static void launch_fast_hier(const DecodeArgs& a, const HierArgs& h, hipStream_t s) {
+  const int lookup_blocks = a.B * a.Hq * h.p;
+  hipLaunchKernelGGL((decode_fast_main_hier<D, G, kDecodePrefetch>), dim3(unsigned(lookup_blocks + a.n_waves / 4)),
+                     dim3(256), 0, s, a, h, lookup_blocks);
+  hipLaunchKernelGGL((decode_fast_combine<G>), dim3((a.B * a.Hq + 3) / 4), dim3(256), 0, s, a);
+}
+
+template <int D, int G>
 static void launch_fast(const DecodeArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((decode_fast_main<D, G, kDecodePrefetch>), dim3(a.n_waves / 4), dim3(256), 0, s, a);
   hipLaunchKernelGGL((decode_fast_combine<G>), dim3((a.B * a.Hq + 3) / 4), dim3(256), 0, s, a);
@@ -632,6 +662,28 @@ hipError_t launch_decode_fast(const DecodeArgs& a, hipStream_t s) {
       case 2: launch_fast<64, 2>(a, s); break;
       case 4: launch_fast<64, 4>(a, s); break;
       default: launch_fast<64, 8>(a, s); break;
+    }
+  }
+  return hipGetLastError();
+}
+
+bool hier_fast_path(int dtype, int d) { return dtype == 0 && (d == 64 || d == 128); }
+
+hipError_t launch_decode_hier(const DecodeArgs& a, const HierArgs& h, hipStream_t s) {
+  const int G = a.Hq / a.Hkv;
+  if (a.d == 128) {
+    switch (G) {
+      case 1: launch_fast_hier<128, 1>(a, h, s); break;
+      case 2: launch_fast_hier<128, 2>(a, h, s); break;
+      case 4: launch_fast_hier<128, 4>(a, h, s); break;
+      default: launch_fast_hier<128, 8>(a, h, s); break;
+    }
+  } else {
+    switch (G) {
+      case 1: launch_fast_hier<64, 1>(a, h, s); break;
+      case 2: launch_fast_hier<64, 2>(a, h, s); break;
+      case 4: launch_fast_hier<64, 4>(a, h, s); break;
+      default: launch_fast_hier<64, 8>(a, h, s); break;
     }
   }
   return hipGetLastError();

@@ -1,4 +1,5 @@
-// Two-level (hierarchical) retrieval for the decode step (bf16, d in {64, 128}).
+// Two-level (hierarchical) retrieval for the decode step (bf16, d in {64, 128}):
+// the per-workgroup lookup, run by the lookup blocks of decode_fast_main_hier.
 //
 // Source: "Context Memorization for Efficient Long Context Generation"
 // (technical summary), Fase de Inferencia Online -- Recuperación (nearest
@@ -9,7 +10,7 @@
 // non-empty ones and takes the entry of highest cosine among their members;
 // probing every super is the flat search.
 //
-// One workgroup per (sequence, query head, probe rank r), r < p:
+// One 256-thread workgroup per (sequence, query head, probe rank r), r < p:
 //   1. the query goes to LDS as float32;
 //   2. each thread scores up to four supers (a dot product over its 16-byte
 //      row pieces against the query in LDS) into (score, index) keys, kept
@@ -22,12 +23,14 @@
 //      (head, sequence) where the flat search writes its unit keys.  The
 //      flat path's merge kernel reduces the p units to the entry, and its
 //      attention kernel runs unchanged with scoring switched off.
+#pragma once
+
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace asmk {
 
-namespace {
+namespace hier {
 
 constexpr int kThreads = 256;
 constexpr int kSupersPerThread = 4;
@@ -59,17 +62,18 @@ __device__ __forceinline__ uint64_t block_max_u64(uint64_t v, uint64_t* red) {
   return m;
 }
 
-}  // namespace
+}  // namespace hier
 
+// The lookup of one workgroup (block index blk of the lookup grid).
 template <int D>
-__global__ void __launch_bounds__(kThreads) hier_lookup_kernel(HierArgs a) {
+__device__ __forceinline__ void hier_lookup_block(const HierArgs& a, int blk) {
   __shared__ float qs[D];
   __shared__ uint64_t keys_s[kHierMaxSupers];
   __shared__ uint64_t red[4];
   __shared__ int32_t probe_s;
   const int t = threadIdx.x;
-  const int r = blockIdx.x % a.p;        // probe rank of this workgroup
-  const int item = blockIdx.x / a.p;     // b * Hq + h
+  const int r = blk % a.p;        // probe rank of this workgroup
+  const int item = blk / a.p;     // b * Hq + h
   const int b = item / a.Hq, h = item % a.Hq;
 
   const uint16_t* qp = static_cast<const uint16_t*>(a.q) + size_t(item) * D;
@@ -80,19 +84,19 @@ __global__ void __launch_bounds__(kThreads) hier_lookup_kernel(HierArgs a) {
   const uint16_t* SC = static_cast<const uint16_t*>(a.SC) + size_t(h) * a.S * D;
   const float* scinv = a.scinv + size_t(h) * a.S;
   const int32_t* off = a.offsets + size_t(h) * (a.S + 1);
-  uint64_t sk[kSupersPerThread];
+  uint64_t sk[hier::kSupersPerThread];
 #pragma unroll
-  for (int i = 0; i < kSupersPerThread; ++i) {
-    const int s = t + kThreads * i;
+  for (int i = 0; i < hier::kSupersPerThread; ++i) {
+    const int s = t + hier::kThreads * i;
     sk[i] = 0ull;
     if (s < a.S && off[s + 1] > off[s])
-      sk[i] = argmax_key(dot_row<D>(SC + size_t(s) * D, qs) * scinv[s], uint32_t(s));
+      sk[i] = argmax_key(hier::dot_row<D>(SC + size_t(s) * D, qs) * scinv[s], uint32_t(s));
     if (s < a.S) keys_s[s] = sk[i];
   }
   __syncthreads();
   // rank of each of this thread's supers among the non-empty ones
 #pragma unroll
-  for (int i = 0; i < kSupersPerThread; ++i) {
+  for (int i = 0; i < hier::kSupersPerThread; ++i) {
     if (sk[i] == 0ull) continue;
     int rank = 0;
     for (int s2 = 0; s2 < a.S; ++s2) rank += keys_s[s2] > sk[i] ? 1 : 0;
@@ -107,27 +111,16 @@ __global__ void __launch_bounds__(kThreads) hier_lookup_kernel(HierArgs a) {
     const float* cinv = a.cinv + size_t(h) * a.K;
     const int32_t* mem = a.members + size_t(h) * a.K + off[probe];
     const int n = off[probe + 1] - off[probe];
-    for (int j = t; j < n; j += kThreads) {
+    for (int j = t; j < n; j += hier::kThreads) {
       const int e = mem[j];
-      best = umax64(best, argmax_key(dot_row<D>(C + size_t(e) * D, qs) * cinv[e], uint32_t(e)));
+      best = umax64(best, argmax_key(hier::dot_row<D>(C + size_t(e) * D, qs) * cinv[e], uint32_t(e)));
     }
   }
-  best = block_max_u64(best, red);
+  best = hier::block_max_u64(best, red);
   if (t == 0) {
     a.keys[(size_t(h) * a.B + b) * a.p + r] = best;
     if (a.probes_out != nullptr) a.probes_out[size_t(item) * a.p + r] = probe;
   }
-}
-
-bool hier_fast_path(int dtype, int d) { return dtype == 0 && (d == 64 || d == 128); }
-
-hipError_t launch_hier_lookup(const HierArgs& a, hipStream_t s) {
-  const dim3 grid(unsigned(a.B * a.Hq * a.p));
-  if (a.d == 128)
-    hipLaunchKernelGGL(hier_lookup_kernel<128>, grid, dim3(kThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL(hier_lookup_kernel<64>, grid, dim3(kThreads), 0, s, a);
-  return hipGetLastError();
 }
 
 }  // namespace asmk

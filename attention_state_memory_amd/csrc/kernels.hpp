@@ -70,7 +70,8 @@ struct HierArgs {
   int32_t* probes_out;  // [B, Hq, p] nullable
 };
 bool hier_fast_path(int dtype, int d);
-hipError_t launch_hier_lookup(const HierArgs& a, hipStream_t s);
+// the main grid with the lookup fused in (MFMA path only), then the combine
+hipError_t launch_decode_hier(const DecodeArgs& a, const HierArgs& h, hipStream_t s);
 
 // ---- whitening at retrieval ---------------------------------------------------
 struct WhitenFitArgs {
