@@ -412,11 +412,11 @@ __device__ __forceinline__ void main_block(const DecodeArgs& a, int blk) {
   // the scoring share, which does not need them.
   const int v_first = (int(threadIdx.x) < a.B && seq_valid(a, threadIdx.x)) ? (a.kv_len[threadIdx.x] + 31) >> 5 : 0;
 
-  // scoring share first: every wave scores at the same time, so the table
-  // streams with the whole grid's memory parallelism
-  // When the grid has a wave for every unit (small steps, which are latency-
-  // bound), the scoring units go to the last SU waves and the attention tiles
-  // to the first ones, so that no wave does both one after the other.
+  // Scoring share first: every wave scores at the same time, so the table
+  // streams with the whole grid's memory parallelism.  When the grid has a
+  // wave for every unit (small steps, which are latency-bound), the scoring
+  // units go to the last SU waves and the attention tiles to the first ones,
+  // so that no wave does both one after the other.
   const int64_t Umax = int64_t(a.B) * a.Hkv * ((int64_t(a.max_kv_len) + 31) / 32);
   if (SU + Umax <= W) {
     const int64_t su = gw - (W - SU);
