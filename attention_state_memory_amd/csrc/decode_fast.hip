@@ -37,6 +37,16 @@ namespace {
 __device__ __forceinline__ int64_t share_lo(int64_t w, int64_t total, int64_t W) {
   return w * total / W;
 }
+// Waves that take attention tiles: all of them, unless the scoring work is
+// the larger part and the grid is capped, in which case the first waves
+// attend and the rest score, in proportion to the two amounts of work.
+__device__ __forceinline__ int64_t attention_waves(const DecodeArgs& a, int64_t W) {
+  const int64_t SU = int64_t(a.Hq) * a.score_uph;
+  const int64_t Umax = int64_t(a.B) * a.Hkv * ((int64_t(a.max_kv_len) + 31) / 32);
+  if (SU + Umax <= W || Umax >= SU) return W;
+  const int64_t A = W * Umax / (SU + Umax);
+  return A < 1 ? 1 : A;
+}
 // the wave whose share holds unit x (inverse of share_lo)
 __device__ __forceinline__ int64_t wave_of(int64_t x, int64_t total, int64_t W) {
   return ((x + 1) * W - 1) / total;
@@ -418,9 +428,13 @@ __device__ __forceinline__ void main_block(const DecodeArgs& a, int blk) {
   // units go to the last SU waves and the attention tiles to the first ones,
   // so that no wave does both one after the other.
   const int64_t Umax = int64_t(a.B) * a.Hkv * ((int64_t(a.max_kv_len) + 31) / 32);
+  const int64_t A = attention_waves(a, W);
   if (SU + Umax <= W) {
     const int64_t su = gw - (W - SU);
     if (su >= 0) score_range<D>(a, int(su), int(su + 1), int(SU));
+  } else if (A < W) {
+    const int64_t gs = gw - A;  // scoring waves A .. W-1
+    if (gs >= 0) score_range<D>(a, int(share_lo(gs, SU, W - A)), int(share_lo(gs + 1, SU, W - A)), int(SU));
   } else {
     score_range<D>(a, int(share_lo(gw, SU, W)), int(share_lo(gw + 1, SU, W)), int(SU));
   }
@@ -454,7 +468,7 @@ __device__ __forceinline__ void main_block(const DecodeArgs& a, int blk) {
   // share holds at least one tile and the pieces of a segment sit at
   // consecutive indices.
   float* pl = pls + w * 32 * G;
-  const int64_t Wa = min(W, U);
+  const int64_t Wa = min(A, U);
   int64_t t = gw < Wa ? share_lo(gw, U, Wa) : 0;
   const int64_t t_end = gw < Wa ? share_lo(gw + 1, U, Wa) : 0;
   while (t < t_end) {
@@ -522,7 +536,7 @@ __global__ void __launch_bounds__(256) decode_fast_combine(DecodeArgs a) {
   int64_t p0 = 0, np = 0;  // pieces of segment (b, g)
   if (nt > 0) {
     const int64_t total = int64_t(tpB) * a.Hkv;
-    const int64_t W = min<int64_t>(a.n_waves, total);
+    const int64_t W = min<int64_t>(attention_waves(a, a.n_waves), total);
     const int64_t first = int64_t(tpb) * a.Hkv + int64_t(g) * nt;
     const int64_t seg = int64_t(b) * a.Hkv + g;
     p0 = wave_of(first, total, W) + seg;
