@@ -155,6 +155,17 @@ def test_decode_batch_beyond_one_launch():
     check_decode(inp, out, lse, idx)
 
 
+@pytest.mark.parametrize("lens", [[2048], [1500, 0, 2600]], ids=["b1", "b3"])
+def test_decode_scoring_dominated_capped_grid(lens):
+    """K = 8192 with one to three short sequences: the scoring units outnumber
+    the attention tiles and the grid is capped at the resident waves, so the
+    first waves take the tiles and the rest the scoring units, in proportion.
+    The lookup and the merge must be the oracle's, as everywhere."""
+    inp = _case(40 + len(lens), 128, 32, 8, 8192, lens)
+    out, lse, idx = run_decode_gpu(inp)
+    check_decode(inp, out, lse, idx)
+
+
 def test_decode_one_sequence_long_context_many_pieces():
     """Batch 1 with a 40000-token context: the segment is split over many
     waves (dozens of partial states merged by the combine)."""
