@@ -521,7 +521,10 @@ decode_fast_main_hier(DecodeArgs a, HierArgs h, int lookup_blocks) {
 template <int G>
 __global__ void __launch_bounds__(256) decode_fast_combine(DecodeArgs a) {
   const int lane = threadIdx.x & 63;
-  const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
+  // wave-uniform values stay in scalar registers (so the loads of the
+  // sequence bounds are scalar and the piece buffer resource needs no
+  // per-lane waterfall loop)
+  const int item = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (item >= a.B * a.Hq) return;
   const int b = item / a.Hq, h = item % a.Hq;
   const int g = h / G, hh = h % G;
@@ -543,7 +546,7 @@ __global__ void __launch_bounds__(256) decode_fast_combine(DecodeArgs a) {
     np = wave_of(first + nt - 1, total, W) + seg - p0 + 1;
   }
   best = wave_max_u64(best);
-  const uint32_t k = key_index(best);
+  const uint32_t k = __builtin_amdgcn_readfirstlane(key_index(best));
   if (lane == 0 && a.out_idx) a.out_idx[item] = int32_t(k);
   float* o = a.out + size_t(item) * D;
   const int dd = 2 * lane;
