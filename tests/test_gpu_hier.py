@@ -162,3 +162,19 @@ def test_decode_hier_one_entry_per_super_with_one_probe():
     ref, ref_lse = O.decode_with_idx(q64, idx, widen(inp["Abar"]), widen(inp["LSEbar"]), ks, vs,
                                      inp["scale"])
     assert_states_close(out, lse, ref, ref_lse)
+
+
+def test_decode_hier_batch_beyond_resident_grid():
+    """40 sequences x 32 heads x 8 probes = 10240 lookup workgroups, more than
+    the device holds at once, ahead of the attention workgroups in the same
+    grid: every lookup and output must still follow the oracle."""
+    r = np.random.default_rng([404, 0])
+    lens = r.integers(0, 300, 40).tolist()
+    inp = _hier_case(5, B=40, Hq=32, Hkv=8, K=2048, S=64, lens=lens)
+    p = 8
+    index, out, lse, idx, probes = _run_hier(inp, S=64, p=p, iters=2)
+    _check_hier(inp, index, idx, probes, p)
+    ks, vs = local_lists(inp)
+    ref, ref_lse = O.decode_with_idx(widen(inp["q"]), idx, widen(inp["Abar"]), widen(inp["LSEbar"]),
+                                     ks, vs, inp["scale"])
+    assert_states_close(out, lse, ref, ref_lse)
