@@ -38,7 +38,7 @@ struct AssignSmem {
 
 template <int D>
 __device__ __forceinline__ void stage_tile(char* buf, __amdgpu_buffer_rsrc_t rc,
-                                           __amdgpu_buffer_rsrc_t ri, int k0,
+                                           __amdgpu_buffer_rsrc_t ri, int k0, int K,
                                            u32x4 (&reg)[kTileCols * D * 2 / 16 / 256], float& ci) {
   // global -> registers: chunk c of the tile is row c / (D/8), 16-byte piece c % (D/8)
   constexpr int kChunksPerRow = D / 8;
@@ -49,7 +49,8 @@ __device__ __forceinline__ void stage_tile(char* buf, __amdgpu_buffer_rsrc_t rc,
     const int row = c / kChunksPerRow, piece = c % kChunksPerRow;
     reg[i] = buf16(rc, ((k0 + row) * D + piece * 8) * 2, 0);
   }
-  ci = threadIdx.x < kTileCols ? buf_f32(ri, (k0 + threadIdx.x) * 4, 0) : 0.0f;
+  // columns past K get a NaN inverse norm: their scores are NaN and never win
+  ci = threadIdx.x < kTileCols ? (k0 + int(threadIdx.x) < K ? buf_f32(ri, (k0 + threadIdx.x) * 4, 0) : __builtin_nanf("")) : 0.0f;
   (void)buf;
 }
 
@@ -111,15 +112,14 @@ assign_mfma_kernel(AssignArgs a, int row_blocks, int per_xcd) {
   const int ntiles = (a.K + kTileCols - 1) / kTileCols;
   u32x4 reg[kPer];
   float ci;
-  stage_tile<D>(smem, rc, ri, 0, reg, ci);
+  stage_tile<D>(smem, rc, ri, 0, a.K, reg, ci);
   commit_tile<D>(smem, reg, ci);
   for (int kt = 0; kt < ntiles; ++kt) {
     __syncthreads();  // tile kt is in buffer kt % 2; buffer (kt+1) % 2 is free
     char* cur = smem + (kt & 1) * AssignSmem<D>::kBufBytes;
     char* nxt = smem + ((kt + 1) & 1) * AssignSmem<D>::kBufBytes;
-    if (kt + 1 < ntiles) stage_tile<D>(nxt, rc, ri, (kt + 1) * kTileCols, reg, ci);
+    if (kt + 1 < ntiles) stage_tile<D>(nxt, rc, ri, (kt + 1) * kTileCols, a.K, reg, ci);
     const float* cil = reinterpret_cast<const float*>(cur + AssignSmem<D>::kTileBytes);
-    const bool partial = (kt + 1) * kTileCols > a.K;
 #pragma unroll 1  // unrolling raises the register count past three waves per SIMD
     for (int ct = 0; ct < kTileCols / 16; ++ct) {
       // B operand: centroid column ct*16 + r16, d chunk 32*s + 8*grp
@@ -130,7 +130,6 @@ assign_mfma_kernel(AssignArgs a, int row_blocks, int per_xcd) {
                                                           (32 * s + 8 * grp) * 2));
       const int col = kt * kTileCols + ct * 16 + r16;
       const float cv = cil[ct * 16 + r16];
-      const bool live = !partial || col < a.K;
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -142,7 +141,7 @@ assign_mfma_kernel(AssignArgs a, int row_blocks, int per_xcd) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float sc = acc[i] * cv;
-          const bool take = live && sc > best[rt][i];
+          const bool take = sc > best[rt][i];
           best[rt][i] = take ? sc : best[rt][i];
           bidx[rt][i] = take ? col : bidx[rt][i];
         }
