@@ -250,6 +250,11 @@ def test_build_states_chunked_equals_monolithic_and_gqa():
                 sc = s[:, c * chunk:(c + 1) * chunk]
                 np.testing.assert_allclose(Lc[c, h], scipy.special.logsumexp(sc, axis=1),
                                            rtol=1e-12)
+                # each chunk's own output: softmax over that chunk's keys only,
+                # not the running state merged so far
+                vc = Vp[g, c * chunk:(c + 1) * chunk]
+                np.testing.assert_allclose(Ac[c, h], scipy.special.softmax(sc, axis=1) @ vc,
+                                           rtol=1e-11, atol=1e-12)
     # empty prefix
     Ac, Lc, A, LSE = O.build_states(np.ones((2, 3, 4)), np.zeros((1, 0, 4)),
                                     np.zeros((1, 0, 4)), 8, 0.5)
@@ -646,3 +651,29 @@ def test_lookup_whitened_identity_transform_is_plain_lookup():
     idx0, cs0, _ = O.assign(q, C)
     np.testing.assert_array_equal(idx, idx0)
     np.testing.assert_array_equal(cs, cs0)
+
+
+def test_lookup_whitened_hand_worked_2d(golden_dir):
+    """A whitened lookup with mu != 0 and W != I, worked by hand, where the
+    plain lookup, whitening one side only, whitening without centring and
+    Sigma^-1 in place of Sigma^-1/2 each pick a different entry."""
+    g = json.load(open(os.path.join(golden_dir, "whiten_lookup_2d_hand.json")))
+    mu_fit, W_fit = O.whiten_fit(np.array(g["corpus"], float), ridge=0.0)
+    np.testing.assert_allclose(mu_fit, g["mu"], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(W_fit, g["W"], rtol=0, atol=1e-14)
+    q, C = np.array([g["q"]], float), np.array(g["C"], float)
+    mu, W = np.array(g["mu"], float), np.array(g["W"], float)
+    for dtype in ("bf16", "f32"):
+        np.testing.assert_array_equal(O.whiten_rows(q, mu, W, dtype), [g["whitened_q"]])
+        np.testing.assert_array_equal(O.whiten_rows(C, mu, W, dtype), g["whitened_C"])
+        idx, cs = O.lookup_whitened(q, C, mu, W, dtype)
+        assert idx[0] == g["idx"]
+        np.testing.assert_allclose(cs[0], g["cos"], rtol=0, atol=1e-15)
+    # the case discriminates: each plausible slip picks another entry
+    qw, Cw = O.whiten_apply(q, mu, W), O.whiten_apply(C, mu, W)
+    assert O.assign(q, C)[0][0] == g["plain_idx"] != g["idx"]
+    assert O.assign(qw, C)[0][0] == g["query_only_idx"] != g["idx"]
+    assert O.assign(q, Cw)[0][0] == g["table_only_idx"] != g["idx"]
+    assert O.assign(q @ W.T, C @ W.T)[0][0] == g["uncentred_idx"] != g["idx"]
+    Winv = W @ W
+    assert O.assign((q - mu) @ Winv.T, (C - mu) @ Winv.T)[0][0] == g["inverse_covariance_idx"] != g["idx"]
