@@ -83,14 +83,6 @@ struct DecodePlan {
   size_t off_keys = 0, off_tp = 0, off_pa = 0, off_pl = 0, total = 0;
 };
 
-int env_int(const char* name, int fallback) {
-  if (const char* e = getenv(name)) {
-    const int v = atoi(e);
-    if (v > 0) return v;
-  }
-  return fallback;
-}
-
 int device_cus() {
   int dev = 0, n = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 256;
@@ -100,8 +92,6 @@ int device_cus() {
 }
 
 int decode_split_tokens(int B, int Hkv, int max_kv_len) {
-  const int v = env_int("ASM_DECODE_SPLIT", 0);
-  if (v >= 32 && v % 32 == 0) return v;
   // about 2048 attention items per step
   const int64_t work = int64_t(B) * Hkv * max_kv_len;
   int64_t s = (work + 2047) / 2048;
@@ -117,7 +107,7 @@ DecodePlan plan_decode(int dtype, int B, int Hq, int Hkv, int d, int K, int max_
                        int64_t kv_tok_stride, int keys_given = 0) {
   DecodePlan p;
   const int G = Hq / Hkv;
-  p.fast = asmk::decode_fast_path(dtype, d, G, kv_tok_stride, max_kv_len);
+  p.fast = asmk::decode_fast_path(dtype, d, G, K, kv_tok_stride, max_kv_len);
   size_t off = 0;
   if (p.fast) {
     p.Bc = B < asmk::kFastMaxBatch ? B : asmk::kFastMaxBatch;
@@ -129,15 +119,16 @@ DecodePlan plan_decode(int dtype, int B, int Hq, int Hkv, int d, int K, int max_
     const int64_t units = int64_t(Hq) * p.score_uph + int64_t(p.Bc) * Hkv * ((int64_t(max_kv_len) + 31) / 32);
     const int64_t cap = int64_t(device_cus()) * asmk::decode_fast_waves_per_cu(d, G);
     int64_t w = units;
-    w = env_int("ASM_DECODE_WAVES", int(w < cap ? w : cap));
-    if (w < 1) w = 1;
-    w = (w + 3) / 4 * 4;
+    w = w < cap ? w : cap;
+    if (w < 2) w = 2;
+    w = (w + asmk::kMainWaves - 1) / asmk::kMainWaves * asmk::kMainWaves;
     p.n_waves = int(w);
     p.off_keys = off;
     off = asmk::align_up(off + size_t(Hq) * p.Bc * p.uph * sizeof(uint64_t), kAlign);
     p.off_tp = off;
     off = asmk::align_up(off + size_t(p.Bc + 1) * sizeof(int32_t), kAlign);
-    const size_t pieces = size_t(p.n_waves) + size_t(p.Bc) * Hkv;
+    // one partial state per (rank, segment), two per rank when ranks are wave pairs
+    const size_t pieces = size_t(p.n_waves) + 2 * size_t(p.Bc) * Hkv;
     p.off_pa = off;
     off = asmk::align_up(off + pieces * G * d * sizeof(float), kAlign);
     p.off_pl = off;

@@ -51,11 +51,32 @@ constexpr int kBufferFlags = 0x00020000;  // raw buffer, 32-bit data format
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t num_bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, int(num_bytes), kBufferFlags);
 }
+// Marks a wave-uniform pointer as such, so that buffer resources built from
+// it live in scalar registers (otherwise every load through them becomes a
+// per-lane waterfall loop).
+template <typename T>
+__device__ __forceinline__ T* uniform_ptr(T* p) {
+  const uint64_t u = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(u));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(u >> 32));
+  return reinterpret_cast<T*>((uint64_t(hi) << 32) | lo);
+}
 __device__ __forceinline__ u32x4 buf16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
 }
 __device__ __forceinline__ float buf_f32(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
   return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+}
+// The same loads with the non-temporal hint (cache-policy bit nt): for data
+// read once per call (the centroid table, the local K/V), which should not
+// displace reused lines.  A plain read stream of a few hundred MB runs about
+// 12% faster this way on gfx950.
+constexpr int kNonTemporal = 2;
+__device__ __forceinline__ u32x4 buf16_nt(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kNonTemporal);
+}
+__device__ __forceinline__ float buf_f32_nt(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, kNonTemporal));
 }
 
 // Round a float64 to bf16, nearest with ties to even, in one step (no

@@ -14,13 +14,19 @@
 //                  heads of the group score the tile on MFMA, the online
 //                  softmax runs on base-2 logits and the value sum on the
 //                  fp32 VALU.
-// decode_fast_main is a persistent grid of n_waves waves.  The scoring units
-// and the attention tiles (in (sequence, kv head, token) order) are each cut
-// into n_waves equal contiguous shares; every wave scores its share first,
-// then attends its tiles, so ragged sequences cost no imbalance.  Each wave
-// writes one partial state per (sequence, kv head) segment it touches.  decode_fast_combine (one wave per (b, h))
-// reduces the keys to the index, gathers the memory state and merges it
-// with the segment's partial states.
+// decode_fast_main is a persistent grid of 8-wave workgroups (two waves per
+// SIMD).  Waves w and w + 4 of a workgroup form a pair; each pair either
+// scores or attends, the two roles in proportion to the bytes they stream, so
+// the table and the local KV stream side by side.  A pair's units (tiles in
+// (sequence, kv head, token) order) are one contiguous pool; its first wave
+// takes them from the front and the second from the back, each claiming the
+// next one from a counter in LDS, so the wave the SIMD serves first (which
+// streams well ahead of its sibling) does more of the pool and both finish
+// together.  Every wave of an attending pair writes one partial state per
+// (sequence, kv head) segment of the pool (an empty one where it attended no
+// tile).  decode_fast_combine (one wave per (b, h)) reduces the keys to the
+// index, gathers the memory state and merges it with the segment's partial
+// states.
 #include <atomic>
 
 #include "common.hpp"
@@ -29,23 +35,54 @@
 
 namespace asmk {
 
-// Issue the next tile's loads before consuming the current one.
-constexpr bool kDecodePrefetch = true;
 
 namespace {
 
 __device__ __forceinline__ int64_t share_lo(int64_t w, int64_t total, int64_t W) {
   return w * total / W;
 }
-// Waves that take attention tiles: all of them, unless the scoring work is
-// the larger part and the grid is capped, in which case the first waves
-// attend and the rest score, in proportion to the two amounts of work.
-__device__ __forceinline__ int64_t attention_waves(const DecodeArgs& a, int64_t W) {
+// How the W waves of the grid divide the step, given U attention tiles and SU
+// scoring units (both known once the lengths are scanned).  The main kernel
+// and the combine evaluate it on the same integers, so they agree on where
+// every partial state lives.
+//   disjoint  the grid has a wave for every unit (small, latency-bound
+//             steps): one unit per wave, attention tiles on waves [0, U),
+//             scoring units on waves [W - SU, W); ranks are waves;
+//   otherwise the W / 2 wave pairs split into S scoring pairs and
+//             W / 2 - S attending pairs so that both roles take about as
+//             long.  The memory system is saturated, so a wave's rate is
+//             proportional to the bytes it keeps in flight: an attending
+//             wave keeps two tiles, a scoring wave two half units (about
+//             half as many bytes), so a unit weighs two tiles, and is
+//             scored once per 32 sequences.  The scoring pairs are spread
+//             evenly: pair p scores iff floor((p+1) S / P) > floor(p S / P).
+//             Ranks are pairs; the first Wa attending ranks hold the
+//             tiles.
+struct Roles {
+  int64_t S;   // scoring pairs (disjoint: scoring waves)
+  int64_t Wa;  // attention ranks that hold tiles
+  bool disjoint;
+};
+__device__ __forceinline__ Roles plan_roles(const DecodeArgs& a, int64_t W, int64_t U) {
   const int64_t SU = int64_t(a.Hq) * a.score_uph;
-  const int64_t Umax = int64_t(a.B) * a.Hkv * ((int64_t(a.max_kv_len) + 31) / 32);
-  if (SU + Umax <= W || Umax >= SU) return W;
-  const int64_t A = W * Umax / (SU + Umax);
-  return A < 1 ? 1 : A;
+  if (SU + U <= W) return {SU, U, true};
+  const int64_t P = W / 2;
+  int64_t S = 0;
+  if (U == 0) {
+    S = P;
+  } else if (SU > 0) {
+    const int64_t ub = U;
+    const int64_t sb = 2 * SU * ((int64_t(a.B) + 31) / 32);
+    S = (P * sb + (ub + sb) / 2) / (ub + sb);
+    S = S < 1 ? 1 : (S > P - 1 ? P - 1 : S);
+  }
+  return {S, min(P - S, U), false};
+}
+// Partial-state slot of rank r's piece of segment seg: one per rank
+// (disjoint) or one per wave of the pair (member m).  The slots of one
+// segment are consecutive.
+__device__ __forceinline__ int64_t piece_slot(bool disjoint, int64_t r, int64_t seg, int m) {
+  return disjoint ? r + seg : 2 * (r + seg) + m;
 }
 // the wave whose share holds unit x (inverse of share_lo)
 __device__ __forceinline__ int64_t wave_of(int64_t x, int64_t total, int64_t W) {
@@ -63,13 +100,15 @@ __device__ __forceinline__ bool seq_valid(const DecodeArgs& a, int b) {
 // ---------------------------------------------------------------------------
 // A unit is consumed as two halves of 32 centroids.  What one half reads
 // besides the queries: 32 centroid rows and their inverse norms, with a
-// single round trip.  Rows past K read as zeros through the buffer bounds; a
-// half index past the wave's share loads nothing.
+// single round trip.  The half's first row moves the base of its buffer
+// resources (scalar arithmetic), so the per-lane offsets are loop-invariant;
+// rows past K read as zeros through the buffer bounds, and a half index past
+// the wave's share loads nothing.
 template <int D>
 struct ScoreHalf {
   static constexpr int KS = D / 32;
   u32x4 c[2][KS];  // A operand: centroid rows of two 16-row tiles
-  float cv[2][4];  // inverse norms of rows 4*grp + i of each tile
+  f32x4 cv[2];     // inverse norms of rows 4*grp .. 4*grp + 3 of each tile
 };
 
 // half v covers centroids 32*(v % (2*uph)) .. +32 of head v / (2*uph)
@@ -81,18 +120,18 @@ __device__ __forceinline__ void load_half(ScoreHalf<D>& t, const DecodeArgs& a, 
   const bool live = v < SV;
   const int h = live ? v / (2 * a.uph) : 0;
   const int c0 = live ? (v - h * 2 * a.uph) * 32 : 0;
-  const uint32_t cbytes = uint32_t(a.K) * D * 2;
-  const auto rc = make_rsrc(static_cast<const uint16_t*>(a.C) + size_t(h) * a.K * D, cbytes);
-  const auto ri = make_rsrc(a.cinv + size_t(h) * a.K, uint32_t(a.K) * 4);
-  const int cdead = live ? 0 : int(cbytes);
-  const int idead = live ? 0 : a.K * 4;
+  // K * D * 2 < 2^31 on this path; the last unit's second half can start at
+  // or past K (then it reads nothing)
+  const int rows_left = live && a.K > c0 ? a.K - c0 : 0;
+  const char* cb = uniform_ptr(reinterpret_cast<const char*>(static_cast<const uint16_t*>(a.C) + (size_t(h) * a.K + c0) * D));
+  const float* ib = uniform_ptr(a.cinv + size_t(h) * a.K + c0);
+  const auto rc = make_rsrc(cb, uint32_t(rows_left) * D * 2);
+  const auto ri = make_rsrc(ib, uint32_t(rows_left) * 4);
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt) {
-    const int row = c0 + rt * 16 + r16;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) t.c[rt][s] = buf16(rc, (row * D + 32 * s + 8 * grp) * 2 + cdead, 0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) t.cv[rt][i] = buf_f32(ri, (c0 + rt * 16 + 4 * grp + i) * 4 + idead, 0);
+    for (int s = 0; s < KS; ++s) t.c[rt][s] = buf16_nt(rc, ((rt * 16 + r16) * D + 8 * grp) * 2 + 64 * s, 0);
+    t.cv[rt] = __builtin_bit_cast(f32x4, buf16_nt(ri, (rt * 16 + 4 * grp) * 4, 0));
   }
 }
 
@@ -154,34 +193,88 @@ __device__ __forceinline__ void store_keys(const DecodeArgs& a, int h, int j, in
   }
 }
 
-// Units [lo, hi) of this wave.  Units of one head are contiguous; per head
-// (and per slice of 32 sequences) the queries are loaded once and the loop
-// over half units keeps two halves in flight: the next half's loads are
-// issued before the current one is consumed, and are never skipped, so the
-// compiler waits for exactly one half's loads.
+// ---------------------------------------------------------------------------
+// pools of a wave pair
+// ---------------------------------------------------------------------------
+// Units [lo, hi) shared by the two waves of a pair: member 0 takes them from
+// the front, member 1 from the back.  A claim adds one to the pair's counter
+// in LDS and succeeds while the counter was below the pool size, so the two
+// ends never cross and every unit is taken by exactly one wave.  A wave that
+// the SIMD serves faster simply claims more of the pool.
+struct PairPool {
+  int32_t* ctr;   // in LDS, zero before the first claim
+  int64_t lo, hi;
+  int m;          // 0: front, 1: back
+  int64_t taken;  // units this wave has taken
+};
+__device__ __forceinline__ int64_t claim(PairPool& p) {
+  int c = 0;
+  if ((threadIdx.x & 63) == 0) c = atomicAdd(p.ctr, 1);
+  c = __builtin_amdgcn_readfirstlane(c);
+  if (p.lo + c >= p.hi) return -1;
+  const int64_t u = p.m == 0 ? p.lo + p.taken : p.hi - 1 - p.taken;
+  ++p.taken;
+  return u;
+}
+
+// One unit for all sequences, 32 at a time (batches above 32 sequences).
 template <int D>
-__device__ __forceinline__ void score_range(const DecodeArgs& a, int lo, int hi, int SU) {
+__device__ __forceinline__ void score_unit(const DecodeArgs& a, int64_t u, int SV) {
+  const int h = int(u / a.uph), j = int(u - int64_t(h) * a.uph);
+  for (int q0 = 0; q0 < a.B; q0 += 32) {
+    u32x4 qb[2][D / 32];
+    load_queries<D>(qb, a, h, q0);
+    uint64_t best[2] = {0ull, 0ull};
+    ScoreHalf<D> t0, t1;
+    load_half<D>(t0, a, int(2 * u), SV);
+    load_half<D>(t1, a, int(2 * u + 1), SV);
+    consume_half<D>(t0, qb, a, 64 * j, best);
+    consume_half<D>(t1, qb, a, 64 * j + 32, best);
+    store_keys<D>(a, h, j, q0, best);
+  }
+}
+
+// The scoring units this wave claims from its pool.  With at most 32
+// sequences the queries of a head are loaded once per run of units of that
+// head and two halves stay in flight: each half's loads are issued before
+// the previous half is consumed, the next claimed unit's first half while
+// the current unit's second half is consumed (a unit of another head, or
+// none, loads nothing there and starts a new run).  Larger batches score
+// unit by unit.
+template <int D>
+__device__ __forceinline__ void score_pool(const DecodeArgs& a, PairPool& pool, int SU) {
   const int SV = 2 * SU;
-  int u0 = lo;
-  while (u0 < hi) {
-    const int h = u0 / a.uph;
-    const int u1 = min(hi, (h + 1) * a.uph);
-    for (int q0 = 0; q0 < a.B; q0 += 32) {
-      u32x4 qb[2][D / 32];
-      load_queries<D>(qb, a, h, q0);
-      uint64_t best[2] = {0ull, 0ull};
-      ScoreHalf<D> ta, tb;
-      load_half<D>(ta, a, 2 * u0, SV);
-      for (int u = u0; u < u1; ++u) {
-        const int j = u - h * a.uph;
-        load_half<D>(tb, a, 2 * u + 1, SV);
-        consume_half<D>(ta, qb, a, 64 * j, best);
-        load_half<D>(ta, a, u + 1 < u1 ? 2 * u + 2 : SV, SV);
-        consume_half<D>(tb, qb, a, 64 * j + 32, best);
-        store_keys<D>(a, h, j, q0, best);
-      }
+  int64_t u = claim(pool);
+  if (a.B > 32) {
+    while (u >= 0) {
+      score_unit<D>(a, u, SV);
+      u = claim(pool);
     }
-    u0 = u1;
+    return;
+  }
+  while (u >= 0) {
+    const int h = int(u / a.uph);
+    const int64_t hu = int64_t(h) * a.uph;
+    u32x4 qb[2][D / 32];
+    load_queries<D>(qb, a, h, 0);
+    uint64_t best[2] = {0ull, 0ull};
+    ScoreHalf<D> ta, tb;
+    load_half<D>(ta, a, int(2 * u), SV);
+    int64_t cur = u, nxt;
+    for (;;) {
+      load_half<D>(tb, a, int(2 * cur + 1), SV);
+      __builtin_amdgcn_sched_barrier(0);
+      consume_half<D>(ta, qb, a, int(64 * (cur - hu)), best);
+      nxt = claim(pool);
+      const bool same = nxt >= 0 && nxt / a.uph == h;
+      load_half<D>(ta, a, same ? int(2 * nxt) : SV, SV);
+      __builtin_amdgcn_sched_barrier(0);
+      consume_half<D>(tb, qb, a, int(64 * (cur - hu)) + 32, best);
+      store_keys<D>(a, h, int(cur - hu), 0, best);
+      if (!same) break;
+      cur = nxt;
+    }
+    u = nxt;
   }
 }
 
@@ -219,20 +312,32 @@ struct TileOffsets {
   }
 };
 
-// The tile start is added to the per-lane offsets (not passed as the scalar
-// offset) so that the buffer bounds check covers it; a tile start at or past
-// the segment end loads zeros without touching memory.
+// The tile start moves the base of the tile's buffer resources (scalar
+// arithmetic) and shortens their range to what is left of the segment, so the
+// per-lane offsets stay loop-invariant and the loads need no vector address
+// arithmetic: no temporary register can then alias a load still in flight,
+// which would make the compiler drain the prefetch.  Rows past the segment end
+// read as zeros; a start at or past the end loads nothing.
 template <int D, int G>
-__device__ __forceinline__ void load_tile(Tile<D, G>& t, __amdgpu_buffer_rsrc_t rk,
-                                          __amdgpu_buffer_rsrc_t rv, const TileOffsets<D, G>& o,
-                                          int start) {
+__device__ __forceinline__ void load_tile(Tile<D, G>& t, const char* kseg, const char* vseg,
+                                          uint32_t seg_bytes, const TileOffsets<D, G>& o,
+                                          uint32_t start) {
   using T = Tile<D, G>;
+  // signed difference and a maximum (scalar instructions); an unsigned
+  // saturating subtract would only exist as a vector instruction, which
+  // would move the resource into vector registers.  Both values stay
+  // below 2^31 (the fast path bounds the segment span).
+  const int rem = int(seg_bytes) - int(start);
+  const uint32_t left = uint32_t(rem > 0 ? rem : 0);
+  const uint32_t at = rem > 0 ? start : 0u;
+  const auto rk = make_rsrc(kseg + at, left);
+  const auto rv = make_rsrc(vseg + at, left);
 #pragma unroll
   for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-    for (int s = 0; s < T::KS; ++s) t.k[jj][s] = buf16(rk, o.k[jj] + start + 64 * s, 0);
+    for (int s = 0; s < T::KS; ++s) t.k[jj][s] = buf16_nt(rk, o.k[jj] + 64 * s, 0);
 #pragma unroll
-  for (int r = 0; r < T::NR; ++r) t.v[r] = buf16(rv, o.v[r] + start, 0);
+  for (int r = 0; r < T::NR; ++r) t.v[r] = buf16_nt(rv, o.v[r], 0);
 }
 
 template <int D, int G>
@@ -317,20 +422,49 @@ __device__ __forceinline__ void consume_tile(const Tile<D, G>& t, Running<D, G>&
   wave_lds_sync();
 }
 
-template <int D, int G, bool kPrefetch>
-__device__ __forceinline__ void attn_piece(const DecodeArgs& a, int b, int g, int j0, int j1,
-                                           int64_t piece, float* pl) {
+// Segment (sequence b, kv head g) holding global tile x, from the tile
+// prefix in LDS; x0 is the segment's first global tile, nt its tile count.
+struct SegLoc {
+  int b, g, nt;
+  int64_t x0;
+};
+__device__ __forceinline__ SegLoc locate(const DecodeArgs& a, const int32_t* tp, int64_t x) {
+  // LDS reads land in vector registers; readfirstlane marks the (wave-
+  // uniform) values as scalars so the buffer resources built from them stay
+  // in SGPRs (otherwise every buffer load becomes a waterfall loop).
+  int blo = 0, bhi = a.B;  // tp[blo]*Hkv <= x < tp[bhi]*Hkv
+  while (bhi - blo > 1) {
+    const int mid = (blo + bhi) >> 1;
+    if (int64_t(__builtin_amdgcn_readfirstlane(tp[mid])) * a.Hkv <= x) blo = mid; else bhi = mid;
+  }
+  const int tb0 = __builtin_amdgcn_readfirstlane(tp[blo]);
+  const int nt = __builtin_amdgcn_readfirstlane(tp[blo + 1]) - tb0;
+  const int g = int((x - int64_t(tb0) * a.Hkv) / nt);
+  return {blo, g, nt, int64_t(tb0) * a.Hkv + int64_t(g) * nt};
+}
+
+// Attends the tiles of segment L that this wave claims, starting with the
+// already claimed tile x, and writes their partial state to `slot`.  Two
+// register tiles are in flight: each claim's loads are issued before the
+// current tile is consumed.  They are never skipped -- a claim outside the
+// segment (or none) loads from past the segment end, which reads nothing --
+// so the compiler waits for exactly one tile's loads.  Returns the first
+// claimed tile outside the segment, or -1 once the pool is empty.
+template <int D, int G>
+__device__ __forceinline__ int64_t attn_run(const DecodeArgs& a, const SegLoc& L, int64_t x,
+                                            PairPool& pool, int64_t slot, float* pl) {
   using T = Tile<D, G>;
   const int lane = threadIdx.x & 63;
   const int r16 = lane & 15, grp = lane >> 4;
+  const int b = L.b, g = L.g;
   const int n = __builtin_amdgcn_readfirstlane(a.kv_len[b]);
   const int64_t st0 = __builtin_amdgcn_readfirstlane(a.kv_start[b]);
   const int64_t ts = a.kv_tok_stride;
   const uint32_t seg_bytes = uint32_t(n) * uint32_t(ts) * 2u;
-  const auto rk = make_rsrc(static_cast<const uint16_t*>(a.Kl) + g * a.kv_head_stride + st0 * ts, seg_bytes);
-  const auto rv = make_rsrc(static_cast<const uint16_t*>(a.Vl) + g * a.kv_head_stride + st0 * ts, seg_bytes);
+  const char* kseg = uniform_ptr(reinterpret_cast<const char*>(static_cast<const uint16_t*>(a.Kl) + g * a.kv_head_stride + st0 * ts));
+  const char* vseg = uniform_ptr(reinterpret_cast<const char*>(static_cast<const uint16_t*>(a.Vl) + g * a.kv_head_stride + st0 * ts));
   const TileOffsets<D, G> off(ts);
-  const int tile_bytes = 32 * int(ts) * 2;
+  const uint32_t tile_bytes = 32u * uint32_t(ts) * 2u;
   const uint16_t* qp = static_cast<const uint16_t*>(a.q);
   const u32x4 zero = {0u, 0u, 0u, 0u};
   bf16x8 qa[T::KS];  // A operand: head rows r16 < G
@@ -349,26 +483,29 @@ __device__ __forceinline__ void attn_piece(const DecodeArgs& a, int b, int g, in
 #pragma unroll
     for (int e = 0; e < 8; ++e) st.acc[hh][e] = 0.0f;
 
-  if constexpr (kPrefetch) {
-    // Two register tiles in flight.  The prefetch is never skipped (a
-    // finished piece prefetches from past the segment end, which loads
-    // nothing), so the compiler can wait for exactly one tile's loads.
-    const int end_off = int(seg_bytes);
-    Tile<D, G> ta, tb;
-    load_tile<D, G>(ta, rk, rv, off, j0 * tile_bytes);
-    for (int j = j0; j < j1; j += 2) {
-      load_tile<D, G>(tb, rk, rv, off, j + 1 < j1 ? (j + 1) * tile_bytes : end_off);
-      consume_tile<D, G>(ta, st, qa, a.scale2, min(32, n - 32 * j), pl);
-      if (j + 1 >= j1) break;
-      load_tile<D, G>(ta, rk, rv, off, j + 2 < j1 ? (j + 2) * tile_bytes : end_off);
-      consume_tile<D, G>(tb, st, qa, a.scale2, min(32, n - 32 * (j + 1)), pl);
-    }
-  } else {
-    for (int j = j0; j < j1; ++j) {
-      Tile<D, G> t;
-      load_tile<D, G>(t, rk, rv, off, j * tile_bytes);
-      consume_tile<D, G>(t, st, qa, a.scale2, min(32, n - 32 * j), pl);
-    }
+  const int64_t x1 = L.x0 + L.nt;
+  Tile<D, G> ta, tb;
+  int64_t cur = x, nxt;
+  load_tile<D, G>(ta, kseg, vseg, seg_bytes, off, uint32_t(cur - L.x0) * tile_bytes);
+  // The scheduling barriers keep each prefetch issued before the
+  // consumption of the tile already in flight; otherwise the compiler
+  // hoists that tile's matrix instructions above the prefetch and has to
+  // drain every load first.
+  for (;;) {
+    nxt = claim(pool);
+    bool in = nxt >= L.x0 && nxt < x1;
+    load_tile<D, G>(tb, kseg, vseg, seg_bytes, off, in ? uint32_t(nxt - L.x0) * tile_bytes : seg_bytes);
+    __builtin_amdgcn_sched_barrier(0);
+    consume_tile<D, G>(ta, st, qa, a.scale2, min(32, n - 32 * int(cur - L.x0)), pl);
+    if (!in) break;
+    cur = nxt;
+    nxt = claim(pool);
+    in = nxt >= L.x0 && nxt < x1;
+    load_tile<D, G>(ta, kseg, vseg, seg_bytes, off, in ? uint32_t(nxt - L.x0) * tile_bytes : seg_bytes);
+    __builtin_amdgcn_sched_barrier(0);
+    consume_tile<D, G>(tb, st, qa, a.scale2, min(32, n - 32 * int(cur - L.x0)), pl);
+    if (!in) break;
+    cur = nxt;
   }
 
   // wave totals: l over the 16 token lanes, acc over the token subsets
@@ -381,7 +518,7 @@ __device__ __forceinline__ void attn_piece(const DecodeArgs& a, int b, int g, in
 #pragma unroll
       for (int m = T::LPT; m < 64; m <<= 1) st.acc[hh][e] += shfl_xor_f(st.acc[hh][e], m);
   const int dd0 = 8 * (lane % T::LPT);
-  float* pa = a.part_a + size_t(piece) * G * D;
+  float* pa = a.part_a + size_t(slot) * G * D;
 #pragma unroll
   for (int hh = 0; hh < G; ++hh) {
     const float mh = readlane_f(st.m[hh & 3], 16 * (hh >> 2));
@@ -397,53 +534,60 @@ __device__ __forceinline__ void attn_piece(const DecodeArgs& a, int b, int g, in
       *reinterpret_cast<f32x4*>(pa + hh * D + dd0) = o0;
       *reinterpret_cast<f32x4*>(pa + hh * D + dd0 + 4) = o1;
     }
-    if (lane == 0) a.part_lse[size_t(piece) * G + hh] = (mh + __log2f(lh)) * ASM_LN2;
+    if (lane == 0) a.part_lse[size_t(slot) * G + hh] = (mh + __log2f(lh)) * ASM_LN2;
   }
+  return nxt;
+}
+
+// The attention tiles this wave claims from its pool (rank r), one piece per
+// segment it attends; then an empty piece (lse = -inf, the row left as it
+// is) for every other segment of the pool, so that each wave of the pair owns
+// one slot per segment.  A wave's claims run contiguously from its end of
+// the pool, so the segments it attends form one range.
+template <int D, int G>
+__device__ __forceinline__ void attn_pool(const DecodeArgs& a, const int32_t* tp, PairPool& pool,
+                                          int64_t r, bool disjoint, float* pl) {
+  int64_t s_lo = -1, s_hi = -2;  // segments attended
+  int64_t x = claim(pool);
+  while (x >= 0) {
+    const SegLoc L = locate(a, tp, x);
+    const int64_t seg = int64_t(L.b) * a.Hkv + L.g;
+    s_lo = s_lo < 0 ? seg : min(s_lo, seg);
+    s_hi = max(s_hi, seg);
+    x = attn_run<D, G>(a, L, x, pool, piece_slot(disjoint, r, seg, pool.m), pl);
+  }
+  const SegLoc F = locate(a, tp, pool.lo), E = locate(a, tp, pool.hi - 1);
+  const int64_t f = int64_t(F.b) * a.Hkv + F.g, e = int64_t(E.b) * a.Hkv + E.g;
+  const int lane = threadIdx.x & 63;
+  for (int64_t seg = f; seg <= e; ++seg)
+    if ((seg < s_lo || seg > s_hi) && lane < G)
+      a.part_lse[size_t(piece_slot(disjoint, r, seg, pool.m)) * G + lane] = -INFINITY;
 }
 
 }  // namespace
 
 // ---------------------------------------------------------------------------
-// One workgroup (block index blk) of the main grid.
-template <int D, int G, bool kPrefetch>
+// One workgroup (block index blk) of the main grid: 8 waves, two per SIMD.
+template <int D, int G>
 __device__ __forceinline__ void main_block(const DecodeArgs& a, int blk) {
   __shared__ int32_t tp[kFastMaxBatch + 1];
-  __shared__ int32_t wsum[4];
-  __shared__ float pls[4 * 32 * G];
+  __shared__ int32_t wsum[kMainWaves];
+  __shared__ float pls[kMainWaves * 32 * G];
+  __shared__ int32_t ctr[kMainWaves];  // pool counters: one per pair, or one per wave (disjoint)
   // the wave index is uniform across the wave; telling the compiler keeps the
   // work-share arithmetic and the buffer resources in scalar registers
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
-  const int64_t gw = int64_t(blk) * 4 + w;
+  const int64_t gw = int64_t(blk) * kMainWaves + w;
   const int64_t W = a.n_waves;
   const int64_t SU = int64_t(a.Hq) * a.score_uph;
-
-  // The lengths of the first 256 sequences are loaded now and scanned after
-  // the scoring share, which does not need them.
-  const int v_first = (int(threadIdx.x) < a.B && seq_valid(a, threadIdx.x)) ? (a.kv_len[threadIdx.x] + 31) >> 5 : 0;
-
-  // Scoring share first: every wave scores at the same time, so the table
-  // streams with the whole grid's memory parallelism.  When the grid has a
-  // wave for every unit (small steps, which are latency-bound), the scoring
-  // units go to the last SU waves and the attention tiles to the first ones,
-  // so that no wave does both one after the other.
-  const int64_t Umax = int64_t(a.B) * a.Hkv * ((int64_t(a.max_kv_len) + 31) / 32);
-  const int64_t A = attention_waves(a, W);
-  if (SU + Umax <= W) {
-    const int64_t su = gw - (W - SU);
-    if (su >= 0) score_range<D>(a, int(su), int(su + 1), int(SU));
-  } else if (A < W) {
-    const int64_t gs = gw - A;  // scoring waves A .. W-1
-    if (gs >= 0) score_range<D>(a, int(share_lo(gs, SU, W - A)), int(share_lo(gs + 1, SU, W - A)), int(SU));
-  } else {
-    score_range<D>(a, int(share_lo(gw, SU, W)), int(share_lo(gw + 1, SU, W)), int(SU));
-  }
+  if (threadIdx.x < kMainWaves) ctr[threadIdx.x] = 0;
 
   // tiles per kv head of every sequence, exclusive prefix over sequences
   int carry = 0;
-  for (int base = 0; base < a.B; base += 256) {
+  for (int base = 0; base < a.B; base += kMainThreads) {
     const int b = base + threadIdx.x;
-    const int v = base == 0 ? v_first : (b < a.B && seq_valid(a, b)) ? (a.kv_len[b] + 31) >> 5 : 0;
+    const int v = (b < a.B && seq_valid(a, b)) ? (a.kv_len[b] + 31) >> 5 : 0;
     int x = v;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -455,61 +599,78 @@ __device__ __forceinline__ void main_block(const DecodeArgs& a, int blk) {
     int before = carry;
     for (int ww = 0; ww < w; ++ww) before += wsum[ww];
     if (b < a.B) tp[b] = before + x - v;
-    carry += wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    for (int ww = 0; ww < kMainWaves; ++ww) carry += wsum[ww];
     __syncthreads();
   }
   if (threadIdx.x == 0) tp[a.B] = carry;
   __syncthreads();
   if (blk == 0)
-    for (int b = threadIdx.x; b <= a.B; b += 256) a.tile_prefix[b] = tp[b];
+    for (int b = threadIdx.x; b <= a.B; b += kMainThreads) a.tile_prefix[b] = tp[b];
   const int64_t U = int64_t(__builtin_amdgcn_readfirstlane(tp[a.B])) * a.Hkv;
 
-  // Attention shares go to the first min(W, U) waves only, so that every
-  // share holds at least one tile and the pieces of a segment sit at
-  // consecutive indices.
+  // Role of this wave (plan_roles).  Attention pools go to the first Wa
+  // attending ranks only, so that every pool holds at least one tile and the
+  // pieces of a segment sit at consecutive ranks.
+  const Roles ro = plan_roles(a, W, U);
   float* pl = pls + w * 32 * G;
-  const int64_t Wa = min(A, U);
-  int64_t t = gw < Wa ? share_lo(gw, U, Wa) : 0;
-  const int64_t t_end = gw < Wa ? share_lo(gw + 1, U, Wa) : 0;
-  while (t < t_end) {
-    // LDS reads land in vector registers; readfirstlane marks the (wave-
-    // uniform) values as scalars so the buffer resources built from them stay
-    // in SGPRs (otherwise every buffer load becomes a waterfall loop).
-    int blo = 0, bhi = a.B;  // tp[blo]*Hkv <= t < tp[bhi]*Hkv
-    while (bhi - blo > 1) {
-      const int mid = (blo + bhi) >> 1;
-      if (int64_t(__builtin_amdgcn_readfirstlane(tp[mid])) * a.Hkv <= t) blo = mid; else bhi = mid;
+  // the pool of this wave: kind 1 scores, kind 2 attends, kind 0 idles
+  int kind = 0;
+  PairPool pool{&ctr[w], 0, 0, 0, 0};
+  int64_t rank = 0;
+  if (ro.disjoint) {
+    // one unit per wave, in a pool of its own
+    const int64_t su = gw - (W - SU);
+    if (su >= 0) {
+      kind = 1;
+      pool.lo = su;
+      pool.hi = su + 1;
+    } else if (gw < U) {
+      kind = 2;
+      rank = gw;
+      pool.lo = gw;
+      pool.hi = gw + 1;
     }
-    const int b = blo;
-    const int tb0 = __builtin_amdgcn_readfirstlane(tp[b]);
-    const int nt = __builtin_amdgcn_readfirstlane(tp[b + 1]) - tb0;
-    const int64_t off = t - int64_t(tb0) * a.Hkv;
-    const int g = int(off / nt), j0 = int(off % nt);
-    const int cnt = int(min<int64_t>(nt - j0, t_end - t));
-    attn_piece<D, G, kPrefetch>(a, b, g, j0, j0 + cnt, gw + int64_t(b) * a.Hkv + g, pl);
-    t += cnt;
+  } else {
+    const int64_t P = W / 2;
+    const int pw = w % (kMainWaves / 2);
+    const int64_t gp = int64_t(blk) * (kMainWaves / 2) + pw;
+    const int64_t before = gp * ro.S / P;  // scoring pairs below gp
+    pool.ctr = &ctr[pw];
+    pool.m = w / (kMainWaves / 2);
+    if ((gp + 1) * ro.S / P > before) {
+      kind = 1;
+      pool.lo = share_lo(before, SU, ro.S);
+      pool.hi = share_lo(before + 1, SU, ro.S);
+    } else if (gp - before < ro.Wa) {
+      kind = 2;
+      rank = gp - before;
+      pool.lo = share_lo(rank, U, ro.Wa);
+      pool.hi = share_lo(rank + 1, U, ro.Wa);
+    }
   }
+  if (kind == 1) score_pool<D>(a, pool, int(SU));
+  else if (kind == 2) attn_pool<D, G>(a, tp, pool, rank, ro.disjoint, pl);
 }
 
-template <int D, int G, bool kPrefetch>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kPrefetch ? 2 : 3)))
+template <int D, int G>
+__global__ void __launch_bounds__(kMainThreads) __attribute__((amdgpu_waves_per_eu(2)))
 decode_fast_main(DecodeArgs a) {
-  main_block<D, G, kPrefetch>(a, int(blockIdx.x));
+  main_block<D, G>(a, int(blockIdx.x));
 }
 
 // The two-level lookup fused into the main grid: the first lookup_blocks
 // workgroups run the lookup (one per sequence, head and probe rank) and the
-// rest run the attention shares (scoring off).  The two roles share no
+// rest run the attention pools (scoring off).  The two roles share no
 // data inside the kernel -- the lookup writes the unit keys that the combine
 // reduces -- so at small batch they run side by side instead of one launch
 // after the other.
-template <int D, int G, bool kPrefetch>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kPrefetch ? 2 : 3)))
+template <int D, int G>
+__global__ void __launch_bounds__(kMainThreads) __attribute__((amdgpu_waves_per_eu(2)))
 decode_fast_main_hier(DecodeArgs a, HierArgs h, int lookup_blocks) {
   if (int(blockIdx.x) < lookup_blocks)
     hier_lookup_block<D>(h, int(blockIdx.x));
   else
-    main_block<D, G, kPrefetch>(a, int(blockIdx.x) - lookup_blocks);
+    main_block<D, G>(a, int(blockIdx.x) - lookup_blocks);
 }
 
 // One wave per (b, h): index from the unit keys, gather of the memory
@@ -539,11 +700,12 @@ __global__ void __launch_bounds__(256) decode_fast_combine(DecodeArgs a) {
   int64_t p0 = 0, np = 0;  // pieces of segment (b, g)
   if (nt > 0) {
     const int64_t total = int64_t(tpB) * a.Hkv;
-    const int64_t W = min<int64_t>(attention_waves(a, a.n_waves), total);
+    const Roles ro = plan_roles(a, a.n_waves, total);
     const int64_t first = int64_t(tpb) * a.Hkv + int64_t(g) * nt;
     const int64_t seg = int64_t(b) * a.Hkv + g;
-    p0 = wave_of(first, total, W) + seg;
-    np = wave_of(first + nt - 1, total, W) + seg - p0 + 1;
+    const int64_t r0 = wave_of(first, total, ro.Wa), r1 = wave_of(first + nt - 1, total, ro.Wa);
+    p0 = piece_slot(ro.disjoint, r0, seg, 0);
+    np = (ro.disjoint ? 1 : 2) * (r1 - r0 + 1);
   }
   best = wave_max_u64(best);
   const uint32_t k = __builtin_amdgcn_readfirstlane(key_index(best));
@@ -600,9 +762,10 @@ __global__ void __launch_bounds__(256) decode_fast_combine(DecodeArgs a) {
       }
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
+        // an empty piece (weight 0) may hold stale values: skip it
         const float wi = readlane_f(wc, int(c - c64) + i);
-        v0 = fmaf(wi, __uint_as_float(r[i][0]), v0);
-        v1 = fmaf(wi, __uint_as_float(r[i][1]), v1);
+        v0 = wi > 0.0f ? fmaf(wi, __uint_as_float(r[i][0]), v0) : v0;
+        v1 = wi > 0.0f ? fmaf(wi, __uint_as_float(r[i][1]), v1) : v1;
       }
     }
   }
@@ -613,33 +776,35 @@ __global__ void __launch_bounds__(256) decode_fast_combine(DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-bool decode_fast_path(int dtype, int d, int G, int64_t kv_tok_stride, int max_kv_len) {
-  // buffer offsets are 32-bit: one sequence's KV rows must span < 2 GiB
-  const bool fits = int64_t(max_kv_len + 32) * kv_tok_stride * 2 < (int64_t(1) << 31);
+bool decode_fast_path(int dtype, int d, int G, int K, int64_t kv_tok_stride, int max_kv_len) {
+  // buffer offsets are 32-bit: one sequence's KV rows and one head's
+  // centroid rows (plus a 64-row unit past the end) must span < 2 GiB
+  const bool fits = int64_t(max_kv_len + 32) * kv_tok_stride * 2 < (int64_t(1) << 31) &&
+                    (int64_t(K) + 64) * d * 2 < (int64_t(1) << 31);
   return dtype == 0 && (d == 64 || d == 128) && (G == 1 || G == 2 || G == 4 || G == 8) && fits;
 }
 
 template <int D, int G>
 static void launch_fast_hier(const DecodeArgs& a, const HierArgs& h, hipStream_t s) {
   const int lookup_blocks = a.B * a.Hq * h.p;
-  hipLaunchKernelGGL((decode_fast_main_hier<D, G, kDecodePrefetch>), dim3(unsigned(lookup_blocks + a.n_waves / 4)),
-                     dim3(256), 0, s, a, h, lookup_blocks);
+  hipLaunchKernelGGL((decode_fast_main_hier<D, G>), dim3(unsigned(lookup_blocks + a.n_waves / kMainWaves)),
+                     dim3(kMainThreads), 0, s, a, h, lookup_blocks);
   hipLaunchKernelGGL((decode_fast_combine<G>), dim3((a.B * a.Hq + 3) / 4), dim3(256), 0, s, a);
 }
 
 template <int D, int G>
 static void launch_fast(const DecodeArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((decode_fast_main<D, G, kDecodePrefetch>), dim3(a.n_waves / 4), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((decode_fast_main<D, G>), dim3(a.n_waves / kMainWaves), dim3(kMainThreads), 0, s, a);
   hipLaunchKernelGGL((decode_fast_combine<G>), dim3((a.B * a.Hq + 3) / 4), dim3(256), 0, s, a);
 }
 
 template <int D, int G>
 static int occupancy_waves() {
   int blocks = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_fast_main<D, G, kDecodePrefetch>,
-                                                   256, 0) != hipSuccess || blocks < 1)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_fast_main<D, G>, kMainThreads, 0) !=
+          hipSuccess || blocks < 1)
     blocks = 1;
-  return 4 * blocks;
+  return kMainWaves * blocks;
 }
 
 int decode_fast_waves_per_cu(int d, int G) {

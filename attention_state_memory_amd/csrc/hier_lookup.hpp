@@ -10,9 +10,9 @@
 // non-empty ones and takes the entry of highest cosine among their members;
 // probing every super is the flat search.
 //
-// One 256-thread workgroup per (sequence, query head, probe rank r), r < p:
+// One 512-thread workgroup per (sequence, query head, probe rank r), r < p:
 //   1. the query goes to LDS as float32;
-//   2. each thread scores up to four supers (a dot product over its 16-byte
+//   2. each thread scores up to two supers (a dot product over its 16-byte
 //      row pieces against the query in LDS) into (score, index) keys, kept
 //      in LDS; empty supers get no key;
 //   3. each thread counts, for its supers, how many keys are larger: the
@@ -32,8 +32,9 @@ namespace asmk {
 
 namespace hier {
 
-constexpr int kThreads = 256;
-constexpr int kSupersPerThread = 4;
+constexpr int kThreads = 512;  // the workgroup size of the decode main grid
+constexpr int kWaves = kThreads / 64;
+constexpr int kSupersPerThread = (kHierMaxSupers + kThreads - 1) / kThreads;
 
 // q . row over D bf16 values, the query in LDS as float32
 template <int D>
@@ -57,7 +58,9 @@ __device__ __forceinline__ uint64_t block_max_u64(uint64_t v, uint64_t* red) {
   v = wave_max_u64(v);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();
-  const uint64_t m = umax64(umax64(red[0], red[1]), umax64(red[2], red[3]));
+  uint64_t m = red[0];
+#pragma unroll
+  for (int i = 1; i < kWaves; ++i) m = umax64(m, red[i]);
   __syncthreads();
   return m;
 }
@@ -69,7 +72,7 @@ template <int D>
 __device__ __forceinline__ void hier_lookup_block(const HierArgs& a, int blk) {
   __shared__ float qs[D];
   __shared__ uint64_t keys_s[kHierMaxSupers];
-  __shared__ uint64_t red[4];
+  __shared__ uint64_t red[hier::kWaves];
   __shared__ int32_t probe_s;
   const int t = threadIdx.x;
   const int r = blk % a.p;        // probe rank of this workgroup

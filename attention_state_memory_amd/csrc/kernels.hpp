@@ -33,7 +33,7 @@ struct DecodeArgs {
   float* out_lse;
   int32_t* out_idx;
   // MFMA path
-  int n_waves;           // persistent waves (multiple of 4)
+  int n_waves;           // persistent waves (multiple of kMainWaves)
   int uph;               // argmax keys per (head, sequence): ceil(K / 64) units
   int score_uph;         // units per head the main kernel scores: uph, or 0 when
                          // the keys were written beforehand (hierarchical lookup)
@@ -44,12 +44,14 @@ struct DecodeArgs {
   int score_tiles;  // ceil(K / 256)
   // both
   uint64_t* keys;   // MFMA: [Hq, B, uph]; VALU: [Hq, score_tiles, B]
-  float* part_a;    // MFMA: [n_waves + B*Hkv, G, d]; VALU: [B, Hq, S_max, d]
-  float* part_lse;  // MFMA: [n_waves + B*Hkv, G];    VALU: [B, Hq, S_max]
+  float* part_a;    // MFMA: [n_waves + 2*B*Hkv, G, d]; VALU: [B, Hq, S_max, d]
+  float* part_lse;  // MFMA: [n_waves + 2*B*Hkv, G];    VALU: [B, Hq, S_max]
 };
 
 constexpr int kFastMaxBatch = 2048;  // sequences per MFMA-path launch
-bool decode_fast_path(int dtype, int d, int G, int64_t kv_tok_stride, int max_kv_len);
+constexpr int kMainWaves = 8;        // waves per workgroup of the MFMA main grid (two per SIMD)
+constexpr int kMainThreads = 64 * kMainWaves;
+bool decode_fast_path(int dtype, int d, int G, int K, int64_t kv_tok_stride, int max_kv_len);
 int decode_fast_waves_per_cu(int d, int G);  // resident waves per CU of the MFMA main kernel
 hipError_t launch_decode_fast(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t s);
