@@ -172,6 +172,43 @@ __device__ __forceinline__ float row16_sum(float v) {
   return v;
 }
 
+// Maximum and sum over the four 16-lane groups of a wave (lanes j, j+16,
+// j+32, j+48), with the two lane-swap instructions of gfx950 instead of LDS
+// permutes.
+__device__ __forceinline__ float group4_max(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const float y = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  const unsigned v = __float_as_uint(y);
+  const auto t = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
+}
+__device__ __forceinline__ float group4_sum(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const float y = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  const unsigned v = __float_as_uint(y);
+  const auto t = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return __uint_as_float(t[0]) + __uint_as_float(t[1]);
+}
+
+// Transposing LDS read (gfx950 ds_read_b64_tr_b16) of a row-major tile of
+// 16-bit values with `pitch` bytes per row: the matrix-core operand holding,
+// in lane (r16, grp), column 16*dt + r16 of rows kb .. kb+3 followed by rows
+// kb2 .. kb2+3 (kb, kb2 chosen per lane group).  Over one 16-lane group, lane
+// i addresses row kb + i / 4, columns 16*dt + 4*(i % 4) .. +3, and lane j
+// receives column 16*dt + j of the four rows.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+__device__ __forceinline__ u32x4 lds_read_colT(const char* base, int pitch, int dt, int kb, int kb2,
+                                               int r16) {
+  const int roff = (r16 >> 2) * pitch + (16 * dt + 4 * (r16 & 3)) * 2;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + kb * pitch + roff));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + kb2 * pitch + roff));
+  return u32x4{__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
+               __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]};
+}
+
 // Orders LDS traffic between lanes of one wave without a workgroup barrier.
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");

@@ -279,15 +279,32 @@ __device__ __forceinline__ void score_pool(const DecodeArgs& a, PairPool& pool, 
 }
 
 // ---------------------------------------------------------------------------
-// attention: tiles [j0, j1) of segment (b, g), one wave, one partial state
+// attention tiles: 32 tokens of one (sequence, kv head)
 // ---------------------------------------------------------------------------
+// Per tile and wave, everything but the softmax runs on the matrix cores:
+//   S^T = K q^T   (16x16x32 bf16; A = 16 token rows of K, B = the G query
+//                  rows), so lane (r16, grp) holds the scores of head r16 for
+//                  the 8 tokens 4*grp + i and 16 + 4*grp + i, i < 4;
+//   O += P V      (16x16x32 bf16; A = those 8 probabilities of head r16 as
+//                  they lie, the k index running over the 8 tokens; B = V^T,
+//                  the same 8 tokens of one head dimension, read from the
+//                  row-major V tile in LDS by transposing reads).  P is split
+//                  into bf16 high and low parts (two products), so it enters
+//                  with about 16 significant bits while V stays exact.
+// The online softmax keeps a lazy reference per head: it only moves when the
+// tile maximum exceeds it by more than kLazy (base 2), so most tiles rescale
+// nothing and P stays below 2^kLazy.
+constexpr float kLazy = 8.0f;
+
 template <int D, int G>
 struct Tile {
   static constexpr int KS = D / 32;     // MFMA k-steps over the head dim
-  static constexpr int LPT = D / 8;     // lanes per token row in the value pass
-  static constexpr int TPI = 64 / LPT;  // token rows per wave-wide value load
-  static constexpr int NR = 32 / TPI;   // value rows per lane per tile
-  static constexpr int NG = (G + 3) / 4;
+  static constexpr int DT = D / 16;     // 16-dim slabs of the value product
+  static constexpr int LPT = D / 8;     // lanes per token row of a V load
+  static constexpr int TPI = 64 / LPT;  // token rows per wave-wide V load
+  static constexpr int NR = 32 / TPI;   // V rows per lane per tile
+  static constexpr int kVPitch = D * 2 + 32;  // LDS bytes per V row (padded)
+  static constexpr int kVBytes = 32 * kVPitch;
   u32x4 k[2][KS];
   u32x4 v[NR];
 };
@@ -342,82 +359,89 @@ __device__ __forceinline__ void load_tile(Tile<D, G>& t, const char* kseg, const
 
 template <int D, int G>
 struct Running {
-  float m[4], l[4];  // per head row 4*grp + i, base-2
-  float acc[G][8];   // value sums, dims 8*(lane % LPT) .. +8, token subset lane / LPT
+  float m, l;                  // lane (r16, *): reference and partial sum of head r16
+  f32x4 o[Tile<D, G>::DT];     // lane (r16, grp): heads 4*grp + i, dim 16*dt + r16
 };
+
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  const __bf16 a = (__bf16)lo, b = (__bf16)hi;  // nearest even
+  return uint32_t(__builtin_bit_cast(uint16_t, a)) | (uint32_t(__builtin_bit_cast(uint16_t, b)) << 16);
+}
 
 template <int D, int G>
 __device__ __forceinline__ void consume_tile(const Tile<D, G>& t, Running<D, G>& st,
-                                             const bf16x8 (&qa)[D / 32], float scale2,
-                                             int nvalid, float* pl) {
+                                             const bf16x8 (&qb)[D / 32], float scale2,
+                                             int nvalid, char* vlds) {
   using T = Tile<D, G>;
   const int lane = threadIdx.x & 63;
   const int r16 = lane & 15, grp = lane >> 4;
-  const int tsub = lane / T::LPT;
+  // V rows to LDS (row-major, padded); the transposing reads below follow in
+  // the same wave, whose LDS operations complete in order
+  {
+    const int tsub = lane / T::LPT, dd0 = 8 * (lane % T::LPT);
+#pragma unroll
+    for (int r = 0; r < T::NR; ++r)
+      *reinterpret_cast<u32x4*>(vlds + (tsub + T::TPI * r) * T::kVPitch + dd0 * 2) = t.v[r];
+  }
   f32x4 sc[2];
 #pragma unroll
   for (int jj = 0; jj < 2; ++jj) {
     sc[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < T::KS; ++s)
-      sc[jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s], as_bf16x8(t.k[jj][s]), sc[jj], 0, 0, 0);
+      sc[jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(t.k[jj][s]), qb[s], sc[jj], 0, 0, 0);
   }
-  // sc[jj][i]: head row 4*grp + i, token 16*jj + r16 of the tile
-  const bool v0 = r16 < nvalid, v1 = 16 + r16 < nvalid;
-  float alpha[4];
+  // sc[jj][i]: head r16, token 16*jj + 4*grp + i
+  float mt = -INFINITY;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float s0 = v0 ? sc[0][i] * scale2 : -INFINITY;
-    const float s1 = v1 ? sc[1][i] * scale2 : -INFINITY;
-    const float mt = row16_max(fmaxf(s0, s1));
-    const float mn = fmaxf(st.m[i], mt);  // finite: every tile holds a valid token
-    alpha[i] = __builtin_amdgcn_exp2f(st.m[i] - mn);
-    const float p0 = __builtin_amdgcn_exp2f(s0 - mn);
-    const float p1 = __builtin_amdgcn_exp2f(s1 - mn);
-    st.l[i] = st.l[i] * alpha[i] + p0 + p1;
-    st.m[i] = mn;
-    sc[0][i] = p0;
-    sc[1][i] = p1;
-  }
-  if (grp < T::NG) {
+  for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int hh = 4 * grp + i;
-      if (hh < G) {
-        pl[r16 * G + hh] = sc[0][i];
-        pl[(16 + r16) * G + hh] = sc[1][i];
-      }
+      const bool ok = 16 * jj + 4 * grp + i < nvalid;
+      sc[jj][i] = ok ? sc[jj][i] * scale2 : -INFINITY;
+      mt = fmaxf(mt, sc[jj][i]);
     }
-  }
-  float al[G];
+  mt = group4_max(mt);  // finite: every tile holds a valid token
+  const bool up = r16 < G && mt > st.m + kLazy;  // always true on the first tile
+  if (__builtin_amdgcn_ballot_w64(up) != 0) {
+    const float mn = up ? mt : st.m;
+    const float alpha = up ? __builtin_amdgcn_exp2f(st.m - mn) : 1.0f;
+    st.m = mn;
+    st.l *= alpha;
+    // alpha of head 4*grp + i, broadcast from lane 4*grp + i
+    float al[4];
 #pragma unroll
-  for (int hh = 0; hh < G; ++hh) al[hh] = readlane_f(alpha[hh & 3], 16 * (hh >> 2));
+    for (int i = 0; i < 4; ++i) {
+      const float a0 = readlane_f(alpha, i);
+      const float a1 = G > 4 ? readlane_f(alpha, 4 + i) : a0;
+      al[i] = grp == 0 ? a0 : a1;
+    }
+#pragma unroll
+    for (int dt = 0; dt < T::DT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st.o[dt][i] *= al[i];
+  }
+  u32x4 phi, plo;
+  float psum = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    float p[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int jj = (2 * e + h) >> 2, i = (2 * e + h) & 3;
+      p[h] = __builtin_amdgcn_exp2f(sc[jj][i] - st.m);  // masked tokens: 0
+      psum += p[h];
+    }
+    phi[e] = pack_bf16(p[0], p[1]);
+    plo[e] = pack_bf16(p[0] - bf16_lo(phi[e]), p[1] - bf16_hi(phi[e]));
+  }
+  st.l += psum;
   wave_lds_sync();
-  bool rescale = false;
 #pragma unroll
-  for (int hh = 0; hh < G; ++hh) rescale |= (al[hh] != 1.0f);
-  if (rescale) {
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) st.acc[hh][e] *= al[hh];
-  }
-#pragma unroll
-  for (int r = 0; r < T::NR; ++r) {
-    const int tl = tsub + T::TPI * r;
-    float p[G];
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh) p[hh] = pl[tl * G + hh];
-    float v[8];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      v[2 * c] = bf16_lo(t.v[r][c]);
-      v[2 * c + 1] = bf16_hi(t.v[r][c]);
-    }
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) st.acc[hh][e] = fmaf(p[hh], v[e], st.acc[hh][e]);
+  for (int dt = 0; dt < T::DT; ++dt) {
+    const bf16x8 vt = as_bf16x8(lds_read_colT(vlds, T::kVPitch, dt, 4 * grp, 16 + 4 * grp, r16));
+    st.o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(phi), vt, st.o[dt], 0, 0, 0);
+    st.o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(plo), vt, st.o[dt], 0, 0, 0);
   }
   wave_lds_sync();
 }
@@ -452,7 +476,7 @@ __device__ __forceinline__ SegLoc locate(const DecodeArgs& a, const int32_t* tp,
 // claimed tile outside the segment, or -1 once the pool is empty.
 template <int D, int G>
 __device__ __forceinline__ int64_t attn_run(const DecodeArgs& a, const SegLoc& L, int64_t x,
-                                            PairPool& pool, int64_t slot, float* pl) {
+                                            PairPool& pool, int64_t slot, char* vlds) {
   using T = Tile<D, G>;
   const int lane = threadIdx.x & 63;
   const int r16 = lane & 15, grp = lane >> 4;
@@ -467,21 +491,16 @@ __device__ __forceinline__ int64_t attn_run(const DecodeArgs& a, const SegLoc& L
   const uint32_t tile_bytes = 32u * uint32_t(ts) * 2u;
   const uint16_t* qp = static_cast<const uint16_t*>(a.q);
   const u32x4 zero = {0u, 0u, 0u, 0u};
-  bf16x8 qa[T::KS];  // A operand: head rows r16 < G
+  bf16x8 qb[T::KS];  // B operand of the score product: query rows r16 < G
 #pragma unroll
   for (int s = 0; s < T::KS; ++s)
-    qa[s] = as_bf16x8(r16 < G ? ld16(qp + (size_t(b) * a.Hq + g * G + r16) * D + 32 * s + 8 * grp) : zero);
+    qb[s] = as_bf16x8(r16 < G ? ld16(qp + (size_t(b) * a.Hq + g * G + r16) * D + 32 * s + 8 * grp) : zero);
 
   Running<D, G> st;
+  st.m = r16 < G ? -INFINITY : 0.0f;  // lanes past the group hold finite filler
+  st.l = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    st.m[i] = -INFINITY;
-    st.l[i] = 0.0f;
-  }
-#pragma unroll
-  for (int hh = 0; hh < G; ++hh)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) st.acc[hh][e] = 0.0f;
+  for (int dt = 0; dt < T::DT; ++dt) st.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int64_t x1 = L.x0 + L.nt;
   Tile<D, G> ta, tb;
@@ -496,45 +515,37 @@ __device__ __forceinline__ int64_t attn_run(const DecodeArgs& a, const SegLoc& L
     bool in = nxt >= L.x0 && nxt < x1;
     load_tile<D, G>(tb, kseg, vseg, seg_bytes, off, in ? uint32_t(nxt - L.x0) * tile_bytes : seg_bytes);
     __builtin_amdgcn_sched_barrier(0);
-    consume_tile<D, G>(ta, st, qa, a.scale2, min(32, n - 32 * int(cur - L.x0)), pl);
+    consume_tile<D, G>(ta, st, qb, a.scale2, min(32, n - 32 * int(cur - L.x0)), vlds);
     if (!in) break;
     cur = nxt;
     nxt = claim(pool);
     in = nxt >= L.x0 && nxt < x1;
     load_tile<D, G>(ta, kseg, vseg, seg_bytes, off, in ? uint32_t(nxt - L.x0) * tile_bytes : seg_bytes);
     __builtin_amdgcn_sched_barrier(0);
-    consume_tile<D, G>(tb, st, qa, a.scale2, min(32, n - 32 * int(cur - L.x0)), pl);
+    consume_tile<D, G>(tb, st, qb, a.scale2, min(32, n - 32 * int(cur - L.x0)), vlds);
     if (!in) break;
     cur = nxt;
   }
 
-  // wave totals: l over the 16 token lanes, acc over the token subsets
-#pragma unroll
-  for (int i = 0; i < 4; ++i) st.l[i] = row16_sum(st.l[i]);
-#pragma unroll
-  for (int hh = 0; hh < G; ++hh)
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-#pragma unroll
-      for (int m = T::LPT; m < 64; m <<= 1) st.acc[hh][e] += shfl_xor_f(st.acc[hh][e], m);
-  const int dd0 = 8 * (lane % T::LPT);
+  // head totals: the denominator of head r16 summed over the lane groups
+  const float lt = group4_sum(st.l);
   float* pa = a.part_a + size_t(slot) * G * D;
+  float inv[G];
 #pragma unroll
   for (int hh = 0; hh < G; ++hh) {
-    const float mh = readlane_f(st.m[hh & 3], 16 * (hh >> 2));
-    const float lh = readlane_f(st.l[hh & 3], 16 * (hh >> 2));
-    const float inv = 1.0f / lh;
-    if (lane < T::LPT) {
-      f32x4 o0, o1;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        o0[e] = st.acc[hh][e] * inv;
-        o1[e] = st.acc[hh][4 + e] * inv;
-      }
-      *reinterpret_cast<f32x4*>(pa + hh * D + dd0) = o0;
-      *reinterpret_cast<f32x4*>(pa + hh * D + dd0 + 4) = o1;
-    }
+    const float mh = readlane_f(st.m, hh), lh = readlane_f(lt, hh);
+    inv[hh] = 1.0f / lh;
     if (lane == 0) a.part_lse[size_t(slot) * G + hh] = (mh + __log2f(lh)) * ASM_LN2;
+  }
+  // lane (r16, grp) holds heads 4*grp + i, dims 16*dt + r16
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int hh = 4 * grp + i;
+    const float iv = G > 4 ? (grp == 0 ? inv[i & (G - 1)] : inv[(4 + i) & (G - 1)]) : inv[i & (G - 1)];
+    if (hh < G) {
+#pragma unroll
+      for (int dt = 0; dt < T::DT; ++dt) pa[hh * D + 16 * dt + r16] = st.o[dt][i] * iv;
+    }
   }
   return nxt;
 }
@@ -546,7 +557,7 @@ __device__ __forceinline__ int64_t attn_run(const DecodeArgs& a, const SegLoc& L
 // the pool, so the segments it attends form one range.
 template <int D, int G>
 __device__ __forceinline__ void attn_pool(const DecodeArgs& a, const int32_t* tp, PairPool& pool,
-                                          int64_t r, bool disjoint, float* pl) {
+                                          int64_t r, bool disjoint, char* vlds) {
   int64_t s_lo = -1, s_hi = -2;  // segments attended
   int64_t x = claim(pool);
   while (x >= 0) {
@@ -554,7 +565,7 @@ __device__ __forceinline__ void attn_pool(const DecodeArgs& a, const int32_t* tp
     const int64_t seg = int64_t(L.b) * a.Hkv + L.g;
     s_lo = s_lo < 0 ? seg : min(s_lo, seg);
     s_hi = max(s_hi, seg);
-    x = attn_run<D, G>(a, L, x, pool, piece_slot(disjoint, r, seg, pool.m), pl);
+    x = attn_run<D, G>(a, L, x, pool, piece_slot(disjoint, r, seg, pool.m), vlds);
   }
   const SegLoc F = locate(a, tp, pool.lo), E = locate(a, tp, pool.hi - 1);
   const int64_t f = int64_t(F.b) * a.Hkv + F.g, e = int64_t(E.b) * a.Hkv + E.g;
@@ -572,7 +583,7 @@ template <int D, int G>
 __device__ __forceinline__ void main_block(const DecodeArgs& a, int blk) {
   __shared__ int32_t tp[kFastMaxBatch + 1];
   __shared__ int32_t wsum[kMainWaves];
-  __shared__ float pls[kMainWaves * 32 * G];
+  __shared__ __attribute__((aligned(16))) char vls[kMainWaves * Tile<D, G>::kVBytes];  // V tile per wave
   __shared__ int32_t ctr[kMainWaves];  // pool counters: one per pair, or one per wave (disjoint)
   // the wave index is uniform across the wave; telling the compiler keeps the
   // work-share arithmetic and the buffer resources in scalar registers
@@ -612,7 +623,7 @@ __device__ __forceinline__ void main_block(const DecodeArgs& a, int blk) {
   // attending ranks only, so that every pool holds at least one tile and the
   // pieces of a segment sit at consecutive ranks.
   const Roles ro = plan_roles(a, W, U);
-  float* pl = pls + w * 32 * G;
+  char* vl = vls + w * Tile<D, G>::kVBytes;
   // the pool of this wave: kind 1 scores, kind 2 attends, kind 0 idles
   int kind = 0;
   PairPool pool{&ctr[w], 0, 0, 0, 0};
@@ -649,7 +660,7 @@ __device__ __forceinline__ void main_block(const DecodeArgs& a, int blk) {
     }
   }
   if (kind == 1) score_pool<D>(a, pool, int(SU));
-  else if (kind == 2) attn_pool<D, G>(a, tp, pool, rank, ro.disjoint, pl);
+  else if (kind == 2) attn_pool<D, G>(a, tp, pool, rank, ro.disjoint, vl);
 }
 
 template <int D, int G>

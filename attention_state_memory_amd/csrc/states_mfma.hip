@@ -98,24 +98,11 @@ __device__ __forceinline__ void stage_store(char* buf, const Staged<D>& r) {
   }
 }
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-
 // V^T operand of the value MFMA for dims 16*dt .. +15 and the 8 keys
-// {kb .. kb+3} and {kb2 .. kb2+3} (per lane group) of the tile in LDS.  A
-// transposing read over a 16-lane group returns, to lane j, element j % 16
-// of ... four consecutive rows: lane i of the group addresses row
-// kb + i / 4, dims 16*dt + 4*(i % 4) .. +3, and lane j receives dim
-// 16*dt + j of rows kb .. kb+3.
+// {kb .. kb+3} and {kb2 .. kb2+3} (per lane group) of the tile in LDS.
 template <int D>
 __device__ __forceinline__ f16x8 load_vt(const char* vbase, int dt, int kb, int kb2, int r16) {
-  using S = StatesSmem<D>;
-  const int roff = (r16 >> 2) * S::kVRow + (16 * dt + 4 * (r16 & 3)) * 2;
-  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vbase + kb * S::kVRow + roff));
-  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vbase + kb2 * S::kVRow + roff));
-  const u32x4 v = {__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
-                   __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]};
-  return __builtin_bit_cast(f16x8, v);
+  return __builtin_bit_cast(f16x8, lds_read_colT(vbase, StatesSmem<D>::kVRow, dt, kb, kb2, r16));
 }
 
 // bf16 -> fp16 (round to nearest even), eight values per thread
@@ -135,17 +122,6 @@ __global__ void v_to_f16_kernel(const u32x4* src, u32x4* dst, int64_t n8) {
 }
 
 }  // namespace
-
-// Maximum over the four 16-lane groups of a wave (lanes j, j+16, j+32, j+48),
-// with the two lane-swap instructions of gfx950 instead of LDS permutes.
-__device__ __forceinline__ float group4_max(float x) {
-  const unsigned u = __float_as_uint(x);
-  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  const float y = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-  const unsigned v = __float_as_uint(y);
-  const auto t = __builtin_amdgcn_permlane16_swap(v, v, false, false);
-  return fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
-}
 
 // Online softmax of one 64-key tile for query column tile qt: scores
 // st[ks][kk][qt][i] belong to key 32*ks + 16*kk + 4*grp + i.  The reference
