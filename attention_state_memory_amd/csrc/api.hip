@@ -448,6 +448,8 @@ int asm_build_states(int dtype, int Hq, int Hkv, int N, int L, int d, int chunk,
   a.A_chunks = A_chunks; a.LSE_chunks = LSE_chunks; a.A = A; a.LSE = LSE;
   a.accumulate = accumulate ? 1 : 0;
   a.V16 = need > 0 ? ws : nullptr;
+  a.v_overflow = need > 0 ? reinterpret_cast<int*>(static_cast<char*>(ws) + asmk::states_v16_bytes(Hkv, L, d))
+                          : nullptr;
   return hip_status(asmk::launch_build_states(a, dtype, stream), "build_states");
 }
 

@@ -15,15 +15,15 @@
 //                  softmax runs on base-2 logits and the value sum on the
 //                  fp32 VALU.
 // decode_fast_main is a persistent grid of 8-wave workgroups (two waves per
-// SIMD).  Waves w and w + 4 of a workgroup form a pair; each pair either
-// scores or attends, the two roles in proportion to the bytes they stream, so
-// the table and the local KV stream side by side.  A pair's units (tiles in
-// (sequence, kv head, token) order) are one contiguous pool; its first wave
-// takes them from the front and the second from the back, each claiming the
-// next one from a counter in LDS, so the wave the SIMD serves first (which
-// streams well ahead of its sibling) does more of the pool and both finish
-// together.  Every wave of an attending pair writes one partial state per
-// (sequence, kv head) segment of the pool (an empty one where it attended no
+// SIMD).  Waves w and w + 4 of a workgroup form a pair, and every pair gets
+// the same pool: its share of the scoring units followed by its share of the
+// tiles (in (sequence, kv head, token) order), so every compute unit streams
+// the same bytes.  The pair's first wave takes items from the front of the
+// pool and the second from the back, each claiming the next one from a
+// counter in LDS, so the table and the local KV stream side by side and the
+// wave the SIMD serves first (which streams well ahead of its sibling) does
+// more of the pool.  Every wave writes one partial state per (sequence, kv
+// head) segment of its pool's tiles (an empty one where it attended no
 // tile).  decode_fast_combine (one wave per (b, h)) reduces the keys to the
 // index, gathers the memory state and merges it with the segment's partial
 // states.
@@ -48,35 +48,20 @@ __device__ __forceinline__ int64_t share_lo(int64_t w, int64_t total, int64_t W)
 //   disjoint  the grid has a wave for every unit (small, latency-bound
 //             steps): one unit per wave, attention tiles on waves [0, U),
 //             scoring units on waves [W - SU, W); ranks are waves;
-//   otherwise the W / 2 wave pairs split into S scoring pairs and
-//             W / 2 - S attending pairs so that both roles take about as
-//             long.  The memory system is saturated, so a wave's rate is
-//             proportional to the bytes it keeps in flight: an attending
-//             wave keeps two tiles, a scoring wave two half units (about
-//             half as many bytes), so a unit weighs two tiles, and is
-//             scored once per 32 sequences.  The scoring pairs are spread
-//             evenly: pair p scores iff floor((p+1) S / P) > floor(p S / P).
-//             Ranks are pairs; the first Wa attending ranks hold the
-//             tiles.
+//   otherwise every wave pair p < P = W / 2 gets the same mix: scoring units
+//             [p SU / P, (p+1) SU / P) and, for the first Wa = min(P, U)
+//             pairs, tiles [p U / Wa, (p+1) U / Wa).  The memory system
+//             serves every compute unit about equally, so equal bytes per
+//             pair (four pairs per compute unit) make the waves finish
+//             together.  Ranks are pairs.
 struct Roles {
-  int64_t S;   // scoring pairs (disjoint: scoring waves)
-  int64_t Wa;  // attention ranks that hold tiles
+  int64_t Wa;  // ranks that hold tiles
   bool disjoint;
 };
 __device__ __forceinline__ Roles plan_roles(const DecodeArgs& a, int64_t W, int64_t U) {
   const int64_t SU = int64_t(a.Hq) * a.score_uph;
-  if (SU + U <= W) return {SU, U, true};
-  const int64_t P = W / 2;
-  int64_t S = 0;
-  if (U == 0) {
-    S = P;
-  } else if (SU > 0) {
-    const int64_t ub = U;
-    const int64_t sb = 2 * SU * ((int64_t(a.B) + 31) / 32);
-    S = (P * sb + (ub + sb) / 2) / (ub + sb);
-    S = S < 1 ? 1 : (S > P - 1 ? P - 1 : S);
-  }
-  return {S, min(P - S, U), false};
+  if (SU + U <= W) return {U, true};
+  return {min(W / 2, U), false};
 }
 // Partial-state slot of rank r's piece of segment seg: one per rank
 // (disjoint) or one per wave of the pair (member m).  The slots of one
@@ -201,20 +186,26 @@ __device__ __forceinline__ void store_keys(const DecodeArgs& a, int h, int j, in
 // in LDS and succeeds while the counter was below the pool size, so the two
 // ends never cross and every unit is taken by exactly one wave.  A wave that
 // the SIMD serves faster simply claims more of the pool.
+// A pool holds n items: its scoring units first (items [0, nsu), units
+// su_lo ..), then its attention tiles (item nsu + i is tile t_lo + i).
 struct PairPool {
   int32_t* ctr;   // in LDS, zero before the first claim
-  int64_t lo, hi;
+  int64_t n, nsu, su_lo, t_lo;
   int m;          // 0: front, 1: back
-  int64_t taken;  // units this wave has taken
+  int64_t taken;  // items this wave has taken
 };
 __device__ __forceinline__ int64_t claim(PairPool& p) {
   int c = 0;
   if ((threadIdx.x & 63) == 0) c = atomicAdd(p.ctr, 1);
   c = __builtin_amdgcn_readfirstlane(c);
-  if (p.lo + c >= p.hi) return -1;
-  const int64_t u = p.m == 0 ? p.lo + p.taken : p.hi - 1 - p.taken;
+  if (c >= p.n) return -1;
+  const int64_t v = p.m == 0 ? p.taken : p.n - 1 - p.taken;
   ++p.taken;
-  return u;
+  return v;
+}
+__device__ __forceinline__ bool pool_unit(const PairPool& p, int64_t v) { return v >= 0 && v < p.nsu; }
+__device__ __forceinline__ int64_t pool_tile(const PairPool& p, int64_t v) {
+  return v >= p.nsu ? p.t_lo + (v - p.nsu) : -1;
 }
 
 // One unit for all sequences, 32 at a time (batches above 32 sequences).
@@ -234,48 +225,47 @@ __device__ __forceinline__ void score_unit(const DecodeArgs& a, int64_t u, int S
   }
 }
 
-// The scoring units this wave claims from its pool.  With at most 32
-// sequences the queries of a head are loaded once per run of units of that
-// head and two halves stay in flight: each half's loads are issued before
-// the previous half is consumed, the next claimed unit's first half while
-// the current unit's second half is consumed (a unit of another head, or
-// none, loads nothing there and starts a new run).  Larger batches score
-// unit by unit.
+// The run of scoring units this wave claims, starting with the claimed item
+// v (a unit); returns the first claimed item that ends the run (a tile, a
+// unit of another head, or -1).  With at most 32 sequences the queries of
+// the head are loaded once and two halves stay in flight: each half's loads
+// are issued before the previous half is consumed, the next claimed unit's
+// first half while the current unit's second half is consumed (an item that
+// ends the run loads nothing there).  Larger batches score unit by unit.
 template <int D>
-__device__ __forceinline__ void score_pool(const DecodeArgs& a, PairPool& pool, int SU) {
+__device__ __forceinline__ int64_t score_run(const DecodeArgs& a, PairPool& pool, int64_t v, int SU) {
   const int SV = 2 * SU;
-  int64_t u = claim(pool);
   if (a.B > 32) {
-    while (u >= 0) {
-      score_unit<D>(a, u, SV);
-      u = claim(pool);
+    while (pool_unit(pool, v)) {
+      score_unit<D>(a, pool.su_lo + v, SV);
+      v = claim(pool);
     }
-    return;
+    return v;
   }
-  while (u >= 0) {
-    const int h = int(u / a.uph);
-    const int64_t hu = int64_t(h) * a.uph;
-    u32x4 qb[2][D / 32];
-    load_queries<D>(qb, a, h, 0);
-    uint64_t best[2] = {0ull, 0ull};
-    ScoreHalf<D> ta, tb;
-    load_half<D>(ta, a, int(2 * u), SV);
-    int64_t cur = u, nxt;
-    for (;;) {
-      load_half<D>(tb, a, int(2 * cur + 1), SV);
-      __builtin_amdgcn_sched_barrier(0);
-      consume_half<D>(ta, qb, a, int(64 * (cur - hu)), best);
-      nxt = claim(pool);
-      const bool same = nxt >= 0 && nxt / a.uph == h;
-      load_half<D>(ta, a, same ? int(2 * nxt) : SV, SV);
-      __builtin_amdgcn_sched_barrier(0);
-      consume_half<D>(tb, qb, a, int(64 * (cur - hu)) + 32, best);
-      store_keys<D>(a, h, int(cur - hu), 0, best);
-      if (!same) break;
-      cur = nxt;
-    }
-    u = nxt;
+  const int64_t u = pool.su_lo + v;
+  const int h = int(u / a.uph);
+  const int64_t hu = int64_t(h) * a.uph;
+  u32x4 qb[2][D / 32];
+  load_queries<D>(qb, a, h, 0);
+  uint64_t best[2] = {0ull, 0ull};
+  ScoreHalf<D> ta, tb;
+  load_half<D>(ta, a, int(2 * u), SV);
+  int64_t cur = u, nxt;
+  for (;;) {
+    load_half<D>(tb, a, int(2 * cur + 1), SV);
+    __builtin_amdgcn_sched_barrier(0);
+    consume_half<D>(ta, qb, a, int(64 * (cur - hu)), best);
+    nxt = claim(pool);
+    const int64_t un = pool.su_lo + nxt;
+    const bool same = pool_unit(pool, nxt) && un / a.uph == h;
+    load_half<D>(ta, a, same ? int(2 * un) : SV, SV);
+    __builtin_amdgcn_sched_barrier(0);
+    consume_half<D>(tb, qb, a, int(64 * (cur - hu)) + 32, best);
+    store_keys<D>(a, h, int(cur - hu), 0, best);
+    if (!same) break;
+    cur = un;
   }
+  return nxt;
 }
 
 // ---------------------------------------------------------------------------
@@ -468,15 +458,16 @@ __device__ __forceinline__ SegLoc locate(const DecodeArgs& a, const int32_t* tp,
 }
 
 // Attends the tiles of segment L that this wave claims, starting with the
-// already claimed tile x, and writes their partial state to `slot`.  Two
-// register tiles are in flight: each claim's loads are issued before the
-// current tile is consumed.  They are never skipped -- a claim outside the
-// segment (or none) loads from past the segment end, which reads nothing --
-// so the compiler waits for exactly one tile's loads.  Returns the first
-// claimed tile outside the segment, or -1 once the pool is empty.
+// already claimed tile x (pool item v), and writes their partial state to
+// `slot`.  Two register tiles are in flight: each claim's loads are issued
+// before the current tile is consumed.  They are never skipped -- a claim
+// outside the segment (or none) loads from past the segment end, which reads
+// nothing -- so the compiler waits for exactly one tile's loads.  Returns
+// the first claimed item outside the segment, or -1 once the pool is empty.
 template <int D, int G>
 __device__ __forceinline__ int64_t attn_run(const DecodeArgs& a, const SegLoc& L, int64_t x,
                                             PairPool& pool, int64_t slot, char* vlds) {
+  int64_t nv;  // pool item of the next claim
   using T = Tile<D, G>;
   const int lane = threadIdx.x & 63;
   const int r16 = lane & 15, grp = lane >> 4;
@@ -511,14 +502,16 @@ __device__ __forceinline__ int64_t attn_run(const DecodeArgs& a, const SegLoc& L
   // hoists that tile's matrix instructions above the prefetch and has to
   // drain every load first.
   for (;;) {
-    nxt = claim(pool);
+    nv = claim(pool);
+    nxt = pool_tile(pool, nv);
     bool in = nxt >= L.x0 && nxt < x1;
     load_tile<D, G>(tb, kseg, vseg, seg_bytes, off, in ? uint32_t(nxt - L.x0) * tile_bytes : seg_bytes);
     __builtin_amdgcn_sched_barrier(0);
     consume_tile<D, G>(ta, st, qb, a.scale2, min(32, n - 32 * int(cur - L.x0)), vlds);
     if (!in) break;
     cur = nxt;
-    nxt = claim(pool);
+    nv = claim(pool);
+    nxt = pool_tile(pool, nv);
     in = nxt >= L.x0 && nxt < x1;
     load_tile<D, G>(ta, kseg, vseg, seg_bytes, off, in ? uint32_t(nxt - L.x0) * tile_bytes : seg_bytes);
     __builtin_amdgcn_sched_barrier(0);
@@ -547,32 +540,40 @@ __device__ __forceinline__ int64_t attn_run(const DecodeArgs& a, const SegLoc& L
       for (int dt = 0; dt < T::DT; ++dt) pa[hh * D + 16 * dt + r16] = st.o[dt][i] * iv;
     }
   }
-  return nxt;
+  return nv;
 }
 
-// The attention tiles this wave claims from its pool (rank r), one piece per
-// segment it attends; then an empty piece (lse = -inf, the row left as it
-// is) for every other segment of the pool, so that each wave of the pair owns
-// one slot per segment.  A wave's claims run contiguously from its end of
-// the pool, so the segments it attends form one range.
+// Everything this wave claims from its pool (rank r): runs of scoring units
+// and one attention piece per segment it attends; then an empty piece (lse =
+// -inf, the row left as it is) for every other segment of the pool's tiles,
+// so that each wave of the pair owns one slot per segment.  A wave's claims
+// run contiguously from its end of the pool, so the segments it attends
+// form one range.
 template <int D, int G>
-__device__ __forceinline__ void attn_pool(const DecodeArgs& a, const int32_t* tp, PairPool& pool,
-                                          int64_t r, bool disjoint, char* vlds) {
+__device__ __forceinline__ void run_pool(const DecodeArgs& a, const int32_t* tp, PairPool& pool,
+                                         int64_t r, bool disjoint, int SU, char* vlds) {
   int64_t s_lo = -1, s_hi = -2;  // segments attended
-  int64_t x = claim(pool);
-  while (x >= 0) {
+  int64_t v = claim(pool);
+  while (v >= 0) {
+    if (pool_unit(pool, v)) {
+      v = score_run<D>(a, pool, v, SU);
+      continue;
+    }
+    const int64_t x = pool_tile(pool, v);
     const SegLoc L = locate(a, tp, x);
     const int64_t seg = int64_t(L.b) * a.Hkv + L.g;
     s_lo = s_lo < 0 ? seg : min(s_lo, seg);
     s_hi = max(s_hi, seg);
-    x = attn_run<D, G>(a, L, x, pool, piece_slot(disjoint, r, seg, pool.m), vlds);
+    v = attn_run<D, G>(a, L, x, pool, piece_slot(disjoint, r, seg, pool.m), vlds);
   }
-  const SegLoc F = locate(a, tp, pool.lo), E = locate(a, tp, pool.hi - 1);
-  const int64_t f = int64_t(F.b) * a.Hkv + F.g, e = int64_t(E.b) * a.Hkv + E.g;
-  const int lane = threadIdx.x & 63;
-  for (int64_t seg = f; seg <= e; ++seg)
-    if ((seg < s_lo || seg > s_hi) && lane < G)
-      a.part_lse[size_t(piece_slot(disjoint, r, seg, pool.m)) * G + lane] = -INFINITY;
+  if (pool.n > pool.nsu) {
+    const SegLoc F = locate(a, tp, pool.t_lo), E = locate(a, tp, pool.t_lo + (pool.n - pool.nsu) - 1);
+    const int64_t f = int64_t(F.b) * a.Hkv + F.g, e = int64_t(E.b) * a.Hkv + E.g;
+    const int lane = threadIdx.x & 63;
+    for (int64_t seg = f; seg <= e; ++seg)
+      if ((seg < s_lo || seg > s_hi) && lane < G)
+        a.part_lse[size_t(piece_slot(disjoint, r, seg, pool.m)) * G + lane] = -INFINITY;
+  }
 }
 
 }  // namespace
@@ -624,43 +625,33 @@ __device__ __forceinline__ void main_block(const DecodeArgs& a, int blk) {
   // pieces of a segment sit at consecutive ranks.
   const Roles ro = plan_roles(a, W, U);
   char* vl = vls + w * Tile<D, G>::kVBytes;
-  // the pool of this wave: kind 1 scores, kind 2 attends, kind 0 idles
-  int kind = 0;
-  PairPool pool{&ctr[w], 0, 0, 0, 0};
+  // the pool of this wave (rank: the pair, or the wave when disjoint)
+  PairPool pool{&ctr[w], 0, 0, 0, 0, 0, 0};
   int64_t rank = 0;
   if (ro.disjoint) {
     // one unit per wave, in a pool of its own
     const int64_t su = gw - (W - SU);
     if (su >= 0) {
-      kind = 1;
-      pool.lo = su;
-      pool.hi = su + 1;
+      pool.n = pool.nsu = 1;
+      pool.su_lo = su;
     } else if (gw < U) {
-      kind = 2;
       rank = gw;
-      pool.lo = gw;
-      pool.hi = gw + 1;
+      pool.n = 1;
+      pool.t_lo = gw;
     }
   } else {
     const int64_t P = W / 2;
     const int pw = w % (kMainWaves / 2);
-    const int64_t gp = int64_t(blk) * (kMainWaves / 2) + pw;
-    const int64_t before = gp * ro.S / P;  // scoring pairs below gp
+    rank = int64_t(blk) * (kMainWaves / 2) + pw;
     pool.ctr = &ctr[pw];
     pool.m = w / (kMainWaves / 2);
-    if ((gp + 1) * ro.S / P > before) {
-      kind = 1;
-      pool.lo = share_lo(before, SU, ro.S);
-      pool.hi = share_lo(before + 1, SU, ro.S);
-    } else if (gp - before < ro.Wa) {
-      kind = 2;
-      rank = gp - before;
-      pool.lo = share_lo(rank, U, ro.Wa);
-      pool.hi = share_lo(rank + 1, U, ro.Wa);
-    }
+    pool.su_lo = share_lo(rank, SU, P);
+    pool.nsu = share_lo(rank + 1, SU, P) - pool.su_lo;
+    const int64_t nt = rank < ro.Wa ? share_lo(rank + 1, U, ro.Wa) - share_lo(rank, U, ro.Wa) : 0;
+    pool.t_lo = rank < ro.Wa ? share_lo(rank, U, ro.Wa) : 0;
+    pool.n = pool.nsu + nt;
   }
-  if (kind == 1) score_pool<D>(a, pool, int(SU));
-  else if (kind == 2) attn_pool<D, G>(a, tp, pool, rank, ro.disjoint, vl);
+  run_pool<D, G>(a, tp, pool, rank, ro.disjoint, int(SU), vl);
 }
 
 template <int D, int G>

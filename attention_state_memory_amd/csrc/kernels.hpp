@@ -117,10 +117,12 @@ struct StatesArgs {
   float* A;
   float* LSE;
   int accumulate;
-  void* V16;  // MFMA path: Vp converted to fp16 [Hkv, L, d] (workspace)
+  void* V16;        // MFMA path: Vp converted to fp16 [Hkv, L, d] (workspace)
+  int* v_overflow;  // MFMA path: set when a finite Vp value has no fp16 form (workspace)
 };
 bool states_fast_path(int dtype, int d, int G);
 size_t states_ws_bytes(int dtype, int Hq, int Hkv, int N, int L, int d);  // 0: VALU path
+size_t states_v16_bytes(int Hkv, int L, int d);  // the fp16 V part of that workspace
 hipError_t launch_build_states(const StatesArgs& a, int dtype, hipStream_t s);
 hipError_t launch_states_generic(const StatesArgs& a, int dtype, hipStream_t s);
 

@@ -22,6 +22,7 @@
 // change the result unless a float64 sum is inexact.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "states_generic.hpp"
 
 namespace asmk {
 
@@ -553,81 +554,11 @@ hipError_t launch_assign_generic(const AssignArgs& a, int dtype, hipStream_t s) 
 // ---------------------------------------------------------------------------
 // plain VALU prefix states: one wave per (query head, query)
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void merge_state(float& l1, float* a1, float l2, const float* a2) {
-  const float M = fmaxf(l1, l2);
-  if (M == -INFINITY) return;
-  const float w1 = l1 == -INFINITY ? 0.0f : expf(l1 - M);
-  const float w2 = l2 == -INFINITY ? 0.0f : expf(l2 - M);
-  const float z = w1 + w2;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) a1[j] = (w1 * a1[j] + w2 * a2[j]) / z;
-  l1 = M + logf(z);
-}
-
 template <typename T>
 __global__ void __launch_bounds__(256) states_generic(StatesArgs a) {
-  const int lane = threadIdx.x & 63;
   const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (item >= a.Hq * a.N) return;
-  const int h = item / a.N;
-  const int g = h / (a.Hq / a.Hkv);
-  const int d = a.d;
-  const T* Q = static_cast<const T*>(a.Q);
-  const T* Kg = static_cast<const T*>(a.Kp) + size_t(g) * a.L * d;
-  const T* Vg = static_cast<const T*>(a.Vp) + size_t(g) * a.L * d;
-  float qv[4], ra[4];
-  float rl = -INFINITY;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int x = lane + 64 * j;
-    qv[j] = x < d ? load_elem(Q, size_t(item) * d + x) : 0.0f;
-    ra[j] = (a.accumulate && x < d) ? a.A[size_t(item) * d + x] : 0.0f;
-  }
-  if (a.accumulate) rl = a.LSE[item];
-  for (int c = 0; c < a.nc; ++c) {
-    const int lo = c * a.chunk, hi = min(a.L, lo + a.chunk);
-    float m = -INFINITY, l = 0.0f, acc[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int t = lo; t < hi; ++t) {
-      float s = 0.0f;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int x = lane + 64 * j;
-        if (x < d) s = fmaf(qv[j], load_elem(Kg, size_t(t) * d + x), s);
-      }
-      s = wave_sum(s) * a.scale2;
-      const float mn = fmaxf(m, s);
-      const float al = __builtin_amdgcn_exp2f(m - mn);
-      const float p = __builtin_amdgcn_exp2f(s - mn);
-      l = l * al + p;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int x = lane + 64 * j;
-        const float v = x < d ? load_elem(Vg, size_t(t) * d + x) : 0.0f;
-        acc[j] = fmaf(p, v, acc[j] * al);
-      }
-      m = mn;
-    }
-    float ca[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) ca[j] = acc[j] / l;
-    const float cl = (m + log2f(l)) * ASM_LN2;
-    if (a.A_chunks) {
-      const size_t row = size_t(c) * a.Hq * a.N + item;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int x = lane + 64 * j;
-        if (x < d) a.A_chunks[row * d + x] = ca[j];
-      }
-      if (lane == 0) a.LSE_chunks[row] = cl;
-    }
-    merge_state(rl, ra, cl, ca);
-  }
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int x = lane + 64 * j;
-    if (x < d) a.A[size_t(item) * d + x] = rl == -INFINITY ? 0.0f : ra[j];
-  }
-  if (lane == 0) a.LSE[item] = rl;
+  states_one_query<T>(a, item / a.N, item % a.N);
 }
 
 hipError_t launch_states_generic(const StatesArgs& a, int dtype, hipStream_t s) {

@@ -32,6 +32,7 @@
 // between chunks: every wave reads back only rows it wrote itself.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "states_generic.hpp"
 
 namespace asmk {
 
@@ -105,21 +106,31 @@ __device__ __forceinline__ f16x8 load_vt(const char* vbase, int dt, int kb, int 
   return __builtin_bit_cast(f16x8, lds_read_colT(vbase, StatesSmem<D>::kVRow, dt, kb, kb2, r16));
 }
 
-// bf16 -> fp16 (round to nearest even), eight values per thread
-__global__ void v_to_f16_kernel(const u32x4* src, u32x4* dst, int64_t n8) {
+// bf16 -> fp16 (round to nearest even), eight values per thread.  A finite
+// value of magnitude 65520 or more has no fp16 form (it would become
+// infinity); then the flag is raised and the states kernel takes its exact
+// bf16 path instead.
+__global__ void v_to_f16_kernel(const u32x4* src, u32x4* dst, int64_t n8, int* overflow) {
+  bool ovf = false;
   for (int64_t i = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; i < n8;
        i += int64_t(gridDim.x) * blockDim.x) {
     const u32x4 v = src[i];
     u32x4 o;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const _Float16 lo = (_Float16)bf16_lo(v[e]);
-      const _Float16 hi = (_Float16)bf16_hi(v[e]);
+      const float x0 = bf16_lo(v[e]), x1 = bf16_hi(v[e]);
+      const _Float16 lo = (_Float16)x0;
+      const _Float16 hi = (_Float16)x1;
+      ovf |= (__builtin_isinf(float(lo)) && !__builtin_isinf(x0)) ||
+             (__builtin_isinf(float(hi)) && !__builtin_isinf(x1));
       o[e] = uint32_t(__builtin_bit_cast(uint16_t, lo)) | (uint32_t(__builtin_bit_cast(uint16_t, hi)) << 16);
     }
     dst[i] = o;
   }
+  if (__builtin_amdgcn_ballot_w64(ovf) != 0 && (threadIdx.x & 63) == 0) atomicOr(overflow, 1);
 }
+
+__global__ void clear_flag(int* flag) { *flag = 0; }
 
 }  // namespace
 
@@ -183,6 +194,14 @@ states_mfma_kernel(StatesArgs a, int row_blocks, int hsubs) {
   const int g = blockIdx.x / (row_blocks * hsubs);
   const int h = g * G + hs * GW + (w % GW);
   const int q0 = rb * (kQ * kWaves / GW) + kQ * (w / GW);  // first query of this wave
+
+  // A value with no fp16 form: this wave's queries take the exact bf16 path
+  // (the flag is the same for the whole grid, so no barrier is skipped by
+  // only part of a workgroup).
+  if (__builtin_amdgcn_readfirstlane(*a.v_overflow) != 0) {
+    for (int q = q0; q < q0 + kQ && q < a.N; ++q) states_one_query<uint16_t>(a, h, q);
+    return;
+  }
 
   const auto rk = make_rsrc(static_cast<const uint16_t*>(a.Kp) + size_t(g) * a.L * D, uint32_t(a.L) * D * 2);
   const auto rv = make_rsrc(static_cast<const uint16_t*>(a.V16) + size_t(g) * a.L * D, uint32_t(a.L) * D * 2);
@@ -346,11 +365,13 @@ bool states_fast_path(int dtype, int d, int G) {
   return dtype == 0 && (d == 64 || d == 128) && (G == 1 || G == 2 || G == 4 || G == 8);
 }
 
+size_t states_v16_bytes(int Hkv, int L, int d) { return (size_t(Hkv) * L * d * 2 + 255) / 256 * 256; }
+
 size_t states_ws_bytes(int dtype, int Hq, int Hkv, int N, int L, int d) {
   if (!states_fast_path(dtype, d, Hq / Hkv) || L == 0 || N == 0) return 0;
   if (int64_t(L + kKeys) * d * 2 >= (int64_t(1) << 31) || int64_t(N + kQ * kWaves) * d * 2 >= (int64_t(1) << 31))
     return 0;
-  return (size_t(Hkv) * L * d * 2 + 255) / 256 * 256;
+  return states_v16_bytes(Hkv, L, d) + 256;  // fp16 V, then the overflow flag
 }
 
 template <int D, int GW>
@@ -365,12 +386,14 @@ static void launch_states(const StatesArgs& a, hipStream_t s) {
 
 hipError_t launch_build_states(const StatesArgs& a, int dtype, hipStream_t s) {
   const int G = a.Hq / a.Hkv;
-  if (states_ws_bytes(dtype, a.Hq, a.Hkv, a.N, a.L, a.d) == 0 || a.V16 == nullptr || !(a.scale2 > 0.0f))
+  if (states_ws_bytes(dtype, a.Hq, a.Hkv, a.N, a.L, a.d) == 0 || a.V16 == nullptr ||
+      a.v_overflow == nullptr || !(a.scale2 > 0.0f))
     return launch_states_generic(a, dtype, s);
   const int64_t n8 = int64_t(a.Hkv) * a.L * a.d / 8;
   const int64_t vb = (n8 + 255) / 256;
+  hipLaunchKernelGGL(clear_flag, dim3(1), dim3(1), 0, s, a.v_overflow);
   hipLaunchKernelGGL(v_to_f16_kernel, dim3(unsigned(vb < 8192 ? vb : 8192)), dim3(256), 0, s,
-                     static_cast<const u32x4*>(a.Vp), static_cast<u32x4*>(a.V16), n8);
+                     static_cast<const u32x4*>(a.Vp), static_cast<u32x4*>(a.V16), n8, a.v_overflow);
   if (a.d == 128) {
     if (G == 1) launch_states<128, 1>(a, s);
     else if (G == 2) launch_states<128, 2>(a, s);

@@ -38,6 +38,7 @@ typedef double f64x4 __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 256;
 constexpr int kCovRows = 16;   // rows staged per pass of wh_cov_partial
 constexpr int kGemmK = 16;     // k-slab of the in-workgroup products
+constexpr double kConverged = 1e-6;  // |Z Y - I|_F at which the iteration counts as converged
 
 template <typename T>
 __device__ __forceinline__ double load_d(const T* p, size_t i) {
@@ -234,7 +235,7 @@ __global__ void __launch_bounds__(kThreads) wh_invsqrt(WhitenFitArgs a) {
     prev = res;
     res = sqrt(block_sum_d(r2, red));
     // converged, or stalled at the rounding floor
-    if (res < 1e-14 || (res < 1e-6 && res > 0.5 * prev)) break;
+    if (res < 1e-14 || (res < kConverged && res > 0.5 * prev)) break;
     for (int e = t; e < D * D; e += kThreads)  // T = (3I - P) / 2, in place
       buf[p][e] = (e / D == e % D ? 1.5 : 0.0) - 0.5 * buf[p][e];
     __threadfence_block();
@@ -246,12 +247,15 @@ __global__ void __launch_bounds__(kThreads) wh_invsqrt(WhitenFitArgs a) {
     y = ny;
     z = nz;
   }
-  // W = Z / sqrt(|Sigma|_F), symmetrised
-  const double sc = fro > 0.0 ? 0.5 / sqrt(fro) : 0.0;
+  // W = Z / sqrt(|Sigma|_F), symmetrised.  An iteration that did not
+  // converge (a singular covariance without ridge, a constant corpus) leaves
+  // W as NaN, so nothing downstream can use it unnoticed.
+  const bool converged = res < kConverged && fro > 0.0;
+  const double sc = converged ? 0.5 / sqrt(fro) : NAN;
   double* W = a.W + size_t(h) * D * D;
   for (int e = t; e < D * D; e += kThreads) {
     const int i = e / D, j = e % D;
-    W[e] = (buf[z][i * D + j] + buf[z][j * D + i]) * sc;
+    W[e] = converged ? (buf[z][i * D + j] + buf[z][j * D + i]) * sc : NAN;
   }
   if (t == 0 && a.resid) a.resid[h] = res;
 }

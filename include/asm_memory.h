@@ -167,7 +167,10 @@ int asm_decode_step_hier(int dtype, int B, int Hq, int Hkv, int d, int K, int S,
  *   The inverse square root is the coupled Newton-Schulz iteration in
  *   float64 (at most 100 rounds); resid [H] (float64, nullable) receives
  *   |Z Y - I|_F at exit, about 1e-14 when it converged.  Needs N >= 1 and
- *   ridge >= 0; with ridge = 0 the covariance must be positive definite.
+ *   ridge >= 0.  A head whose iteration does not converge (resid >= 1e-6 or NaN,
+ *   e.g. a singular covariance with ridge = 0, or a constant corpus whose
+ *   covariance is zero) gets W filled with NaN; the call itself still
+ *   returns ASM_OK, since the outcome is only known on the device.
  *   Workspace: asm_whiten_fit_ws bytes.
  * asm_whiten_rows -- Yw = round(W[h] (Y - mu[h])) for M rows of each of H
  *   heads.  Row r of head h starts at element h*head_stride + r*row_stride
@@ -215,10 +218,13 @@ int asm_decode_step_whitened(int dtype, int B, int Hq, int Hkv, int d, int K, fl
  *     prefix streamed in pieces); otherwise they are overwritten.
  *   d in {64, 128} for bf16 (any 1..256 for float32).
  *   bf16 builds with d in {64, 128} and Hq/Hkv in {1, 2, 4, 8} convert Vp
- *   to fp16 once per call into the workspace (asm_build_states_ws bytes,
- *   Hkv*L*d*2 rounded up to 256) and take the probability-value products in
- *   fp16 with float32 accumulation: |Vp| must stay below 65504.  Other
- *   shapes need no workspace.
+ *   to fp16 once per call into the workspace (asm_build_states_ws bytes:
+ *   Hkv*L*d*2 rounded up to 256, plus 256 for a flag) and take the
+ *   probability-value products in fp16 with float32 accumulation.  If some
+ *   finite Vp value has no fp16 form (magnitude 65520 or more), the
+ *   conversion raises the flag and the whole call computes every state on
+ *   the exact bf16 path instead (float32 vector arithmetic, much slower);
+ *   the results stay finite and correct.  Other shapes need no workspace.
  */
 size_t asm_build_states_ws(int dtype, int Hq, int Hkv, int N, int L, int d, int chunk);
 int asm_build_states(int dtype, int Hq, int Hkv, int N, int L, int d, int chunk, float scale,

@@ -93,6 +93,22 @@ def test_workspace_sizes_follow_the_plan():
     assert L.asm_aggregate_ws(0, 32, 65536, 8192, 128) >= 4 * 32 * (65536 + 2 * 8192)
 
 
+def test_decode_table_too_large_for_32_bit_offsets_takes_the_generic_path():
+    """The MFMA decode path addresses one head's centroid rows with 32-bit
+    buffer offsets, so it needs (K + 64) * d * 2 < 2^31; a larger table must
+    be planned on the generic path (workspace: keys [Hq, ceil(K/256), B]
+    u64, partial states [B, Hq, splits, d] and their lse, each padded to
+    256 bytes; one 128-token split for a 64-token local context)."""
+    L = api.lib()
+    d = 128
+    k_big = (1 << 23) - 64  # (K + 64) * 256 == 2^31
+    assert L.asm_decode_step_ws(0, 1, 1, 1, d, k_big, 64) == \
+        ((k_big + 255) // 256) * 8 + 512 + 256
+    # one entry fewer fits the MFMA path, whose workspace differs
+    assert L.asm_decode_step_ws(0, 1, 1, 1, d, k_big - 1, 64) != \
+        ((k_big - 1 + 255) // 256) * 8 + 512 + 256
+
+
 def test_build_assign_aggregate_validation():
     L = api.lib()
     st = L.asm_build_states(0, 4, 3, 8, 16, 128, 4, 0.1, 1 << 20, 1 << 20, 1 << 20, None, None,

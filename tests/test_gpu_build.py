@@ -51,6 +51,39 @@ def test_build_states_matches_oracle(case):
     assert_states_close(host(Ac), host(Lc), Ac_ref, Lc_ref)
 
 
+def test_build_states_values_without_fp16_form_take_the_exact_path():
+    """bf16 values of magnitude 65520 or more have no fp16 form: the MFMA
+    path must notice and compute every state exactly (finite, within the
+    oracle's tolerance scaled by the largest value), and the next call with
+    ordinary values must take the fast path again."""
+    r = _rng(2, 7)
+    Hq, Hkv, N, L, chunk, d = 4, 2, 70, 200, 64, 128
+    Q = synth.to_bf16_bits(r.standard_normal((Hq, N, d), dtype=np.float32))
+    Kp = synth.to_bf16_bits(r.standard_normal((Hkv, L, d), dtype=np.float32))
+    Vf = r.standard_normal((Hkv, L, d), dtype=np.float32)
+    Vf[0, 37, 5] = 2.0 ** 17
+    Vf[1, 150, 90] = -3.0 * 2.0 ** 16
+    Vp = synth.to_bf16_bits(Vf)
+    scale = synth.softmax_scale(d)
+    A, LSE, Ac, Lc = api.build_states(dev(Q), dev(Kp), dev(Vp), chunk, scale, keep_chunks=True)
+    torch.cuda.synchronize()
+    Ac_ref, Lc_ref, A_ref, L_ref = O.build_states(widen(Q), widen(Kp), widen(Vp), chunk, scale)
+    A, Ac = host(A), host(Ac)
+    assert np.isfinite(A).all() and np.isfinite(Ac).all()
+    # float32 accumulation of values up to 2^17: about 2^-24 of the largest
+    tol = 2e-3 + 1e-6 * float(np.abs(widen(Vp)).max())
+    assert np.abs(A - A_ref).max() <= tol
+    assert np.abs(Ac - Ac_ref).max() <= tol
+    assert np.abs(host(LSE) - L_ref).max() <= LSE_TOL
+    assert np.abs(host(Lc) - Lc_ref).max() <= LSE_TOL
+    # ordinary values right after: the flag is cleared per call
+    Vp2 = synth.to_bf16_bits(r.standard_normal((Hkv, L, d), dtype=np.float32))
+    A2, LSE2, _, _ = api.build_states(dev(Q), dev(Kp), dev(Vp2), chunk, scale)
+    torch.cuda.synchronize()
+    _, _, A2_ref, L2_ref = O.build_states(widen(Q), widen(Kp), widen(Vp2), chunk, scale)
+    assert_states_close(host(A2), host(LSE2), A2_ref, L2_ref)
+
+
 def test_build_states_accumulate_and_empty_prefix():
     """Streaming a prefix in two calls (accumulate=1) equals one call over the
     whole prefix; an empty prefix gives empty states."""

@@ -677,3 +677,28 @@ def test_lookup_whitened_hand_worked_2d(golden_dir):
     assert O.assign(q @ W.T, C @ W.T)[0][0] == g["uncentred_idx"] != g["idx"]
     Winv = W @ W
     assert O.assign((q - mu) @ Winv.T, (C - mu) @ Winv.T)[0][0] == g["inverse_covariance_idx"] != g["idx"]
+
+
+def test_whiten_fit_singular_covariance_with_ridge():
+    """Fewer rows than dimensions: the covariance is singular, and only the
+    ridge makes it invertible.  W must then be the symmetric inverse square
+    root of the ridged covariance, W (Sigma + eps I) W = I, with eps =
+    ridge * trace(Sigma) / d; the null directions of Sigma get the factor
+    eps^-1/2 exactly.  Without the ridge the oracle has no finite W."""
+    r = rng(40, 9)
+    N, d = 6, 10
+    X = r.standard_normal((N, d))
+    S0 = np.cov(X.T, bias=True)
+    assert np.linalg.matrix_rank(S0) < d
+    mu, W = O.whiten_fit(X, ridge=1e-6)
+    eps = 1e-6 * np.trace(S0) / d
+    Sr = S0 + eps * np.eye(d)
+    np.testing.assert_allclose(W, W.T, rtol=0, atol=1e-9 * np.abs(W).max())
+    np.testing.assert_allclose(W @ Sr @ W, np.eye(d), rtol=0, atol=1e-6)
+    # a null direction of the centred corpus is scaled by eps^-1/2
+    _, _, Vt = np.linalg.svd(X - X.mean(axis=0))
+    v = Vt[-1]
+    assert abs(np.linalg.norm(W @ v) - eps ** -0.5) <= 1e-6 * eps ** -0.5
+    with np.errstate(all="ignore"):
+        _, W0 = O.whiten_fit(X, ridge=0.0)
+    assert not np.isfinite(W0).all() or np.abs(W0).max() > 1e6
