@@ -33,6 +33,10 @@ SIGNATURES = {
                                  _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                  _c_i64, _c_i64, _c_i64, _vp, _vp, _c_int,
                                  _vp, _vp, _vp, _vp, _c_size, _vp]),
+    "asm_attend_step_ws": (_c_size, [_c_int] * 6),
+    "asm_attend_step": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_float, _vp, _vp, _vp,
+                                 _c_i64, _c_i64, _c_i64, _vp, _vp, _c_int, _vp, _vp, _vp, _c_size,
+                                 _vp]),
     "asm_whiten_fit_ws": (_c_size, [_c_int] * 4),
     "asm_whiten_fit": (_c_int, [_c_int] * 4 + [_vp, ctypes.c_double, _vp, _vp, _vp, _vp, _c_size,
                                                _vp]),
@@ -229,6 +233,39 @@ def whiten_rows(Y, mu, W, *, out=None):
         _dtype_code(Y), H, M, d, _ptr(Y), M * d, d, _ptr(mu), _ptr(W), _ptr(out),
         _stream(Y.device)))
     return out
+
+
+def attend_step(q, Kc, Vc, kv_start, kv_len, max_kv_len: int, scale: float, *, out=None,
+                out_lse=None, workspace=None):
+    """Full attention of one decode step (no memory).  q [B, Hq, d];
+    Kc, Vc [Hkv, capacity, d] (any strides with d contiguous) holding each
+    sequence's whole context; kv_start, kv_len [B] int32 token slots.
+    Returns (out [B, Hq, d] f32, out_lse [B, Hq] f32)."""
+    _dev(q, "q")
+    _dev(kv_start, "kv_start", torch.int32)
+    _dev(kv_len, "kv_len", torch.int32)
+    code = _dtype_code(q)
+    if Kc.dtype != q.dtype or Vc.dtype != q.dtype:
+        raise TypeError("q, Kc and Vc must share one dtype")
+    for t, n in ((Kc, "Kc"), (Vc, "Vc")):
+        if not t.is_cuda or t.dim() != 3 or t.stride(2) != 1:
+            raise ValueError(f"{n} must be a [Hkv, capacity, d] CUDA tensor with d contiguous")
+    if Kc.stride() != Vc.stride() or Kc.shape != Vc.shape:
+        raise ValueError("Kc and Vc must share shape and strides")
+    B, Hq, d = q.shape
+    Hkv, cap, _ = Kc.shape
+    dev = q.device
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+    if out_lse is None:
+        out_lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    nbytes = int(lib().asm_attend_step_ws(code, B, Hq, Hkv, d, int(max_kv_len)))
+    ws = _workspace(nbytes, dev, workspace)
+    _check("asm_attend_step", lib().asm_attend_step(
+        code, B, Hq, Hkv, d, float(scale), _ptr(q), _ptr(Kc), _ptr(Vc), Kc.stride(0), Kc.stride(1),
+        cap, _ptr(kv_start), _ptr(kv_len), int(max_kv_len), _ptr(out), _ptr(out_lse), _ptr(ws),
+        nbytes, _stream(dev)))
+    return out, out_lse
 
 
 def decode_step_whitened(q, mu, W, Cw, cwinv, Abar, LSEbar, Kl, Vl, kv_start, kv_len,

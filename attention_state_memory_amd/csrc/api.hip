@@ -172,12 +172,16 @@ int decode_impl(int dtype, int B, int Hq, int Hkv, int d, int K, float scale,
                 const int32_t* kv_start, const int32_t* kv_len, int max_kv_len,
                 float* out, float* out_lse, int32_t* out_idx,
                 void* ws, size_t ws_bytes, hipStream_t stream, asmk::HierArgs* hier,
-                const void* qs = nullptr) {
+                const void* qs = nullptr, bool attend_only = false) {
   ASM_TRY(validate_decode_shape(dtype, B, Hq, Hkv, d, K, max_kv_len));
   if (!(scale == scale) || scale == INFINITY || scale == -INFINITY)
     return fail(ASM_ERR_SHAPE, "scale must be finite");
-  if (!q || !C || !cinv || !Abar || !LSEbar || !kv_start || !kv_len || !out)
+  if (attend_only) {
+    if (!q || !kv_start || !kv_len || !out)
+      return fail(ASM_ERR_NULL, "q, kv_start, kv_len and out are required");
+  } else if (!q || !C || !cinv || !Abar || !LSEbar || !kv_start || !kv_len || !out) {
     return fail(ASM_ERR_NULL, "q, C, cinv, Abar, LSEbar, kv_start, kv_len and out are required");
+  }
   if (max_kv_len > 0) {
     if (!Kl || !Vl) return fail(ASM_ERR_NULL, "Kl and Vl are required when max_kv_len > 0");
     if (kv_head_stride < 0 || kv_tok_stride < 1 || kv_capacity < 0)
@@ -187,7 +191,11 @@ int decode_impl(int dtype, int B, int Hq, int Hkv, int d, int K, float scale,
   }
   ASM_TRY(check_bf16_ptrs(dtype, {q, C, Kl, Vl}));
   const DecodePlan p = plan_decode(dtype, B, Hq, Hkv, d, K, max_kv_len, kv_tok_stride,
-                                   hier != nullptr ? hier->p : 0);
+                                   hier != nullptr ? hier->p : (attend_only ? 1 : 0));
+  if (attend_only && !p.fast)
+    return fail(ASM_ERR_SHAPE,
+                "attention without memory needs bf16, d in {64, 128}, Hq/Hkv in {1, 2, 4, 8} "
+                "and KV rows of under 2 GiB per sequence");
   if (hier != nullptr && !p.fast)
     return fail(ASM_ERR_SHAPE,
                 "the hierarchical lookup needs bf16, d in {64, 128}, Hq/Hkv in {1, 2, 4, 8} "
@@ -201,6 +209,7 @@ int decode_impl(int dtype, int B, int Hq, int Hkv, int d, int K, float scale,
   a.Kl = Kl; a.Vl = Vl;
   a.kv_head_stride = kv_head_stride; a.kv_tok_stride = kv_tok_stride; a.kv_capacity = kv_capacity;
   a.max_kv_len = max_kv_len;
+  a.no_memory = attend_only ? 1 : 0;
   a.n_waves = p.n_waves; a.uph = p.uph; a.score_uph = p.score_uph;
   a.split_tok = p.split_tok; a.S_max = p.S_max; a.score_tiles = p.score_tiles;
   char* w = static_cast<char*>(ws);
@@ -291,6 +300,23 @@ int asm_decode_step(int dtype, int B, int Hq, int Hkv, int d, int K, float scale
   return decode_impl(dtype, B, Hq, Hkv, d, K, scale, q, C, cinv, Abar, LSEbar, Kl, Vl,
                      kv_head_stride, kv_tok_stride, kv_capacity, kv_start, kv_len, max_kv_len,
                      out, out_lse, out_idx, ws, ws_bytes, stream, nullptr);
+}
+
+// ---------------------------------------------------------------------------
+size_t asm_attend_step_ws(int dtype, int B, int Hq, int Hkv, int d, int max_kv_len) {
+  if (validate_decode_shape(dtype, B, Hq, Hkv, d, 1, max_kv_len) != ASM_OK) return 0;
+  const DecodePlan p = plan_decode(dtype, B, Hq, Hkv, d, 1, max_kv_len, d, 1);
+  return p.fast ? p.total : 0;
+}
+
+int asm_attend_step(int dtype, int B, int Hq, int Hkv, int d, float scale, const void* q,
+                    const void* Kc, const void* Vc, int64_t kv_head_stride, int64_t kv_tok_stride,
+                    int64_t kv_capacity, const int32_t* kv_start, const int32_t* kv_len,
+                    int max_kv_len, float* out, float* out_lse, void* ws, size_t ws_bytes,
+                    hipStream_t stream) {
+  return decode_impl(dtype, B, Hq, Hkv, d, 1, scale, q, nullptr, nullptr, nullptr, nullptr, Kc, Vc,
+                     kv_head_stride, kv_tok_stride, kv_capacity, kv_start, kv_len, max_kv_len,
+                     out, out_lse, nullptr, ws, ws_bytes, stream, nullptr, nullptr, true);
 }
 
 // ---------------------------------------------------------------------------

@@ -697,7 +697,8 @@ __global__ void __launch_bounds__(256) decode_fast_combine(DecodeArgs a) {
   const bool valid = seq_valid(a, b);
   const uint64_t* kk = a.keys + (size_t(h) * a.B + b) * a.uph;
   uint64_t best = 0;
-  for (int u = lane; u < a.uph; u += 64) best = umax64(best, kk[u]);
+  if (!a.no_memory)
+    for (int u = lane; u < a.uph; u += 64) best = umax64(best, kk[u]);
   const int nt = tpb1 - tpb;
   int64_t p0 = 0, np = 0;  // pieces of segment (b, g)
   if (nt > 0) {
@@ -710,7 +711,7 @@ __global__ void __launch_bounds__(256) decode_fast_combine(DecodeArgs a) {
     np = (ro.disjoint ? 1 : 2) * (r1 - r0 + 1);
   }
   best = wave_max_u64(best);
-  const uint32_t k = __builtin_amdgcn_readfirstlane(key_index(best));
+  const uint32_t k = a.no_memory ? 0u : __builtin_amdgcn_readfirstlane(key_index(best));
   if (lane == 0 && a.out_idx) a.out_idx[item] = int32_t(k);
   float* o = a.out + size_t(item) * D;
   const int dd = 2 * lane;
@@ -720,9 +721,10 @@ __global__ void __launch_bounds__(256) decode_fast_combine(DecodeArgs a) {
     return;
   }
   // round 2
-  const float lm = a.LSEbar[size_t(h) * a.K + k];
-  const float2 am = dd < D ? *reinterpret_cast<const float2*>(a.Abar + (size_t(h) * a.K + k) * D + dd)
-                           : make_float2(0.f, 0.f);
+  const float lm = a.no_memory ? -INFINITY : a.LSEbar[size_t(h) * a.K + k];
+  const float2 am = (dd < D && !a.no_memory)
+                        ? *reinterpret_cast<const float2*>(a.Abar + (size_t(h) * a.K + k) * D + dd)
+                        : make_float2(0.f, 0.f);
   const float* pa0 = a.part_a + (p0 * G + hh) * D;
   const auto rp = make_rsrc(pa0, np > 0 ? uint32_t(((np - 1) * G + 1) * D * 4) : 0u);
   // the first 64 piece normalisers and the first 16 piece rows load with the

@@ -38,6 +38,7 @@ struct DecodeArgs {
   int score_uph;         // units per head the main kernel scores: uph, or 0 when
                          // the keys were written beforehand (hierarchical lookup)
   int32_t* tile_prefix;  // [B + 1] 32-token tiles per kv head, prefix over sequences
+  int no_memory;         // attention only: no lookup, the merge starts from the empty state
   // VALU path
   int split_tok;    // local tokens per attention item
   int S_max;        // splits per sequence = ceil(max_kv_len / split_tok)

@@ -127,6 +127,38 @@ def batched_decode(replica: int) -> dict:
                          kv_lens=kv_lens)
 
 
+def attend_inputs(seed, B, Hq, Hkv, d, L, kv_lens, dtype="bf16") -> dict:
+    """A decode step over a fixed L-token prefix plus ragged local contexts,
+    laid out two ways: the local tokens alone (packed head-major as in
+    `decode_inputs`) and every sequence's full context, its own copy of the
+    prefix followed by its local tokens (packed head-major [Hkv, sum(L +
+    n_b), d]).  Draw order: q [B,Hq,d], prefix K then V [Hkv,L,d], local K
+    then V [Hkv,sum(n_b),d]."""
+    rng = np.random.default_rng(seed)
+    kv_lens = np.asarray(kv_lens, dtype=np.int64)
+    total = int(kv_lens.sum())
+    q = _normal(rng, (B, Hq, d))
+    Kp = _normal(rng, (Hkv, L, d))
+    Vp = _normal(rng, (Hkv, L, d))
+    Kl = _normal(rng, (Hkv, total, d))
+    Vl = _normal(rng, (Hkv, total, d))
+    kv_start = np.concatenate([[0], np.cumsum(kv_lens)[:-1]]).astype(np.int64)
+    ctx_len = kv_lens + L
+    ctx_start = np.concatenate([[0], np.cumsum(ctx_len)[:-1]]).astype(np.int64)
+    Kc = np.empty((Hkv, int(ctx_len.sum()), d), np.float32)
+    Vc = np.empty_like(Kc)
+    for b in range(B):
+        c0, l0, n = ctx_start[b], kv_start[b], kv_lens[b]
+        Kc[:, c0:c0 + L], Vc[:, c0:c0 + L] = Kp, Vp
+        Kc[:, c0 + L:c0 + L + n], Vc[:, c0 + L:c0 + L + n] = Kl[:, l0:l0 + n], Vl[:, l0:l0 + n]
+    return dict(dtype=dtype, B=B, Hq=Hq, Hkv=Hkv, d=d, L=L, scale=softmax_scale(d),
+                q=_store(q, dtype), Kp=_store(Kp, dtype), Vp=_store(Vp, dtype),
+                Kl=_store(Kl, dtype), Vl=_store(Vl, dtype),
+                kv_start=kv_start.astype(np.int32), kv_len=kv_lens.astype(np.int32),
+                Kc=_store(Kc, dtype), Vc=_store(Vc, dtype),
+                ctx_start=ctx_start.astype(np.int32), ctx_len=ctx_len.astype(np.int32))
+
+
 # ---------------------------------------------------------------------------
 # build workloads
 # ---------------------------------------------------------------------------

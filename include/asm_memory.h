@@ -63,7 +63,7 @@ enum asm_status_code {
 enum asm_dtype { ASM_BF16 = 0, ASM_F32 = 1 };
 
 /* ABI version of this header (bumped on any signature change). */
-#define ASM_ABI_VERSION 5
+#define ASM_ABI_VERSION 6
 int asm_abi_version(void);
 
 /* Static text for a status code. */
@@ -121,6 +121,28 @@ int asm_decode_step(int dtype, int B, int Hq, int Hkv, int d, int K, float scale
                     const int32_t* kv_start, const int32_t* kv_len, int max_kv_len,
                     float* out, float* out_lse, int32_t* out_idx,
                     void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * asm_attend_step -- full attention of one decode step, without memory: the
+ * baseline the method is timed against ([TS] Resultados Experimentales,
+ * latency against full attention over the prefix; [ABS]).  For every
+ * sequence b and query head h, the attention state of q[b,h] over the
+ * sequence's tokens t = 0..kv_len[b]-1 of kv head g = h / (Hq/Hkv) -- for
+ * the comparison, the prefix followed by the local tokens, one KV cache --
+ * with scores scale * q.k_t:
+ *   out[b,h] = sum_t softmax(s)_t v_t, out_lse[b,h] = log sum_t exp(s_t).
+ * It runs the split-K attention and merge of asm_decode_step with the lookup
+ * switched off and the merge started from the empty state.  Arguments as
+ * asm_decode_step (Kc, Vc take the place of Kl, Vl); kv_len[b] == 0 gives
+ * (0, -inf).  Needs bf16, d in {64, 128}, Hq/Hkv in {1, 2, 4, 8} and each
+ * sequence's rows within 2 GiB; otherwise ASM_ERR_SHAPE (and _ws returns 0).
+ */
+size_t asm_attend_step_ws(int dtype, int B, int Hq, int Hkv, int d, int max_kv_len);
+int asm_attend_step(int dtype, int B, int Hq, int Hkv, int d, float scale, const void* q,
+                    const void* Kc, const void* Vc, int64_t kv_head_stride, int64_t kv_tok_stride,
+                    int64_t kv_capacity, const int32_t* kv_start, const int32_t* kv_len,
+                    int max_kv_len, float* out, float* out_lse, void* ws, size_t ws_bytes,
+                    hipStream_t stream);
 
 /*
  * asm_decode_step_hier -- the decode step with the two-level lookup of an

@@ -41,9 +41,9 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_text():
     L = api.lib()
-    assert L.asm_abi_version() == 5
+    assert L.asm_abi_version() == 6
     text = open(HEADER).read()
-    assert int(re.search(r"#define ASM_ABI_VERSION (\d+)", text).group(1)) == 5
+    assert int(re.search(r"#define ASM_ABI_VERSION (\d+)", text).group(1)) == 6
     assert L.asm_status_str(0) == b"ok"
     assert L.asm_status_str(-5).startswith(b"workspace")
 
