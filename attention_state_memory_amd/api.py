@@ -33,6 +33,10 @@ SIGNATURES = {
                                  _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                  _c_i64, _c_i64, _c_i64, _vp, _vp, _c_int,
                                  _vp, _vp, _vp, _vp, _c_size, _vp]),
+    "asm_decode_step_noalloc": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_float,
+                                         _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                         _c_i64, _c_i64, _c_i64, _vp, _vp, _c_int,
+                                         _vp, _vp, _vp, _vp]),
     "asm_attend_step_ws": (_c_size, [_c_int] * 6),
     "asm_attend_step": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_float, _vp, _vp, _vp,
                                  _c_i64, _c_i64, _c_i64, _vp, _vp, _c_int, _vp, _vp, _vp, _c_size,
@@ -160,13 +164,7 @@ def decode_step_ws(dtype_code: int, B, Hq, Hkv, d, K, max_kv_len) -> int:
     return int(lib().asm_decode_step_ws(dtype_code, B, Hq, Hkv, d, K, max_kv_len))
 
 
-def decode_step(q, C, cinv, Abar, LSEbar, Kl, Vl, kv_start, kv_len, max_kv_len: int,
-                scale: float, *, out=None, out_lse=None, out_idx=None, workspace=None,
-                want_lse: bool = True, want_idx: bool = True):
-    """One decode step.  q [B, Hq, d]; C [Hq, K, d]; cinv, LSEbar [Hq, K];
-    Abar [Hq, K, d]; Kl, Vl [Hkv, capacity, d] (any strides with d
-    contiguous); kv_start, kv_len [B] int32 token slots.
-    Returns (out [B, Hq, d] f32, out_lse [B, Hq] f32 | None, idx [B, Hq] i32 | None)."""
+def _decode_operands(q, C, cinv, Abar, LSEbar, Kl, Vl, kv_start, kv_len):
     for t, n in ((q, "q"), (C, "C")):
         _dev(t, n)
     _dev(cinv, "cinv", torch.float32)
@@ -182,6 +180,17 @@ def decode_step(q, C, cinv, Abar, LSEbar, Kl, Vl, kv_start, kv_len, max_kv_len: 
             raise ValueError(f"{n} must be a [Hkv, capacity, d] CUDA tensor with d contiguous")
     if Kl.stride() != Vl.stride() or Kl.shape != Vl.shape:
         raise ValueError("Kl and Vl must share shape and strides")
+    return code
+
+
+def decode_step(q, C, cinv, Abar, LSEbar, Kl, Vl, kv_start, kv_len, max_kv_len: int,
+                scale: float, *, out=None, out_lse=None, out_idx=None, workspace=None,
+                want_lse: bool = True, want_idx: bool = True):
+    """One decode step.  q [B, Hq, d]; C [Hq, K, d]; cinv, LSEbar [Hq, K];
+    Abar [Hq, K, d]; Kl, Vl [Hkv, capacity, d] (any strides with d
+    contiguous); kv_start, kv_len [B] int32 token slots.
+    Returns (out [B, Hq, d] f32, out_lse [B, Hq] f32 | None, idx [B, Hq] i32 | None)."""
+    code = _decode_operands(q, C, cinv, Abar, LSEbar, Kl, Vl, kv_start, kv_len)
     B, Hq, d = q.shape
     K = C.shape[1]
     Hkv, cap, _ = Kl.shape
@@ -199,6 +208,28 @@ def decode_step(q, C, cinv, Abar, LSEbar, Kl, Vl, kv_start, kv_len, max_kv_len: 
         _ptr(LSEbar), _ptr(Kl), _ptr(Vl), Kl.stride(0), Kl.stride(1), cap,
         _ptr(kv_start), _ptr(kv_len), int(max_kv_len), _ptr(out), _ptr(out_lse), _ptr(out_idx),
         _ptr(ws), nbytes, _stream(dev)))
+    return out, out_lse, out_idx
+
+
+def decode_step_noalloc(q, C, cinv, Abar, LSEbar, Kl, Vl, kv_start, kv_len, max_kv_len: int,
+                        scale: float, *, out, out_lse=None, out_idx=None):
+    """decode_step through the entry point that allocates nothing: the
+    library's fixed per-GPU scratch replaces the workspace, and this binding
+    allocates nothing either (out is required; out_lse and out_idx are
+    written when given).  Returns (out, out_lse, out_idx)."""
+    code = _decode_operands(q, C, cinv, Abar, LSEbar, Kl, Vl, kv_start, kv_len)
+    B, Hq, d = q.shape
+    K = C.shape[1]
+    Hkv, cap, _ = Kl.shape
+    _dev(out, "out", torch.float32)
+    for t, n, dt in ((out_lse, "out_lse", torch.float32), (out_idx, "out_idx", torch.int32)):
+        if t is not None:
+            _dev(t, n, dt)
+    _check("asm_decode_step_noalloc", lib().asm_decode_step_noalloc(
+        code, B, Hq, Hkv, d, K, float(scale), _ptr(q), _ptr(C), _ptr(cinv), _ptr(Abar),
+        _ptr(LSEbar), _ptr(Kl), _ptr(Vl), Kl.stride(0), Kl.stride(1), cap,
+        _ptr(kv_start), _ptr(kv_len), int(max_kv_len), _ptr(out), _ptr(out_lse), _ptr(out_idx),
+        _stream(q.device)))
     return out, out_lse, out_idx
 
 

@@ -6,7 +6,9 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
 #include <initializer_list>
+#include <mutex>
 
 #include "asm_memory.h"
 #include "common.hpp"
@@ -162,17 +164,13 @@ int validate_decode_shape(int dtype, int B, int Hq, int Hkv, int d, int K, int m
   return ASM_OK;
 }
 
-// The decode step for every lookup; `hier` (hierarchical lookup) is NULL for
-// the flat search; `qs` (the queries the lookup scores) is NULL when they are
-// the queries themselves.
-int decode_impl(int dtype, int B, int Hq, int Hkv, int d, int K, float scale,
-                const void* q, const void* C, const float* cinv, const float* Abar,
-                const float* LSEbar, const void* Kl, const void* Vl,
-                int64_t kv_head_stride, int64_t kv_tok_stride, int64_t kv_capacity,
-                const int32_t* kv_start, const int32_t* kv_len, int max_kv_len,
-                float* out, float* out_lse, int32_t* out_idx,
-                void* ws, size_t ws_bytes, hipStream_t stream, asmk::HierArgs* hier,
-                const void* qs = nullptr, bool attend_only = false) {
+// Host checks of a decode step's arguments (no device call).
+int check_decode_args(int dtype, int B, int Hq, int Hkv, int d, int K, float scale, const void* q,
+                      const void* C, const float* cinv, const float* Abar, const float* LSEbar,
+                      const void* Kl, const void* Vl, int64_t kv_head_stride,
+                      int64_t kv_tok_stride, int64_t kv_capacity, const int32_t* kv_start,
+                      const int32_t* kv_len, int max_kv_len, const float* out,
+                      bool attend_only) {
   ASM_TRY(validate_decode_shape(dtype, B, Hq, Hkv, d, K, max_kv_len));
   if (!(scale == scale) || scale == INFINITY || scale == -INFINITY)
     return fail(ASM_ERR_SHAPE, "scale must be finite");
@@ -190,6 +188,23 @@ int decode_impl(int dtype, int B, int Hq, int Hkv, int d, int K, float scale,
       return fail(ASM_ERR_ALIGN, "bf16 kv strides must be multiples of 8 elements");
   }
   ASM_TRY(check_bf16_ptrs(dtype, {q, C, Kl, Vl}));
+  return ASM_OK;
+}
+
+// The decode step for every lookup; `hier` (hierarchical lookup) is NULL for
+// the flat search; `qs` (the queries the lookup scores) is NULL when they are
+// the queries themselves.
+int decode_impl(int dtype, int B, int Hq, int Hkv, int d, int K, float scale,
+                const void* q, const void* C, const float* cinv, const float* Abar,
+                const float* LSEbar, const void* Kl, const void* Vl,
+                int64_t kv_head_stride, int64_t kv_tok_stride, int64_t kv_capacity,
+                const int32_t* kv_start, const int32_t* kv_len, int max_kv_len,
+                float* out, float* out_lse, int32_t* out_idx,
+                void* ws, size_t ws_bytes, hipStream_t stream, asmk::HierArgs* hier,
+                const void* qs = nullptr, bool attend_only = false) {
+  ASM_TRY(check_decode_args(dtype, B, Hq, Hkv, d, K, scale, q, C, cinv, Abar, LSEbar, Kl, Vl,
+                            kv_head_stride, kv_tok_stride, kv_capacity, kv_start, kv_len,
+                            max_kv_len, out, attend_only));
   const DecodePlan p = plan_decode(dtype, B, Hq, Hkv, d, K, max_kv_len, kv_tok_stride,
                                    hier != nullptr ? hier->p : (attend_only ? 1 : 0));
   if (attend_only && !p.fast)
@@ -243,6 +258,50 @@ int decode_impl(int dtype, int B, int Hq, int Hkv, int d, int K, float scale,
     const int st = hip_status(asmk::launch_decode(a, dtype, stream), "decode_step");
     if (st != ASM_OK) return st;
   }
+  return ASM_OK;
+}
+
+// ---- scratch of the no-allocation decode entry point -------------------------
+// One array per GPU, in the code object, so that the entry point needs no
+// allocation.  Host code never uses the array's name as an address: the
+// address on the current device comes from hipGetSymbolAddress, once per
+// device, and is kept in g_scratch.
+constexpr int kMaxScratchDevices = 64;
+std::atomic<void*> g_scratch[kMaxScratchDevices];
+std::mutex g_scratch_mu;
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[ASM_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+// The scratch address on the device of `stream`, which must be the current
+// device.
+int noalloc_scratch(hipStream_t stream, void** out) {
+  int cur = 0, sdev = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return fail(ASM_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  e = hipStreamGetDevice(stream, &sdev);
+  if (e != hipSuccess) return fail(ASM_ERR_HIP, "hipStreamGetDevice: %s", hipGetErrorString(e));
+  if (sdev != cur)
+    return fail(ASM_ERR_SHAPE, "the stream belongs to device %d but device %d is current", sdev, cur);
+  if (cur < 0 || cur >= kMaxScratchDevices)
+    return fail(ASM_ERR_SHAPE, "device %d: the no-allocation entry point serves devices 0..%d", cur,
+                kMaxScratchDevices - 1);
+  void* p = g_scratch[cur].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[cur].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess || p == nullptr)
+        return fail(ASM_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", cur,
+                    hipGetErrorString(e));
+      g_scratch[cur].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
   return ASM_OK;
 }
 
@@ -300,6 +359,31 @@ int asm_decode_step(int dtype, int B, int Hq, int Hkv, int d, int K, float scale
   return decode_impl(dtype, B, Hq, Hkv, d, K, scale, q, C, cinv, Abar, LSEbar, Kl, Vl,
                      kv_head_stride, kv_tok_stride, kv_capacity, kv_start, kv_len, max_kv_len,
                      out, out_lse, out_idx, ws, ws_bytes, stream, nullptr);
+}
+
+// ---------------------------------------------------------------------------
+int asm_decode_step_noalloc(int dtype, int B, int Hq, int Hkv, int d, int K, float scale,
+                            const void* q, const void* C, const float* cinv, const float* Abar,
+                            const float* LSEbar, const void* Kl, const void* Vl,
+                            int64_t kv_head_stride, int64_t kv_tok_stride, int64_t kv_capacity,
+                            const int32_t* kv_start, const int32_t* kv_len, int max_kv_len,
+                            float* out, float* out_lse, int32_t* out_idx, hipStream_t stream) {
+  ASM_TRY(check_decode_args(dtype, B, Hq, Hkv, d, K, scale, q, C, cinv, Abar, LSEbar, Kl, Vl,
+                            kv_head_stride, kv_tok_stride, kv_capacity, kv_start, kv_len,
+                            max_kv_len, out, false));
+  // the layout this call will use (the KV stride picks it), not the larger
+  // of the two that asm_decode_step_ws reports
+  const size_t need = plan_decode(dtype, B, Hq, Hkv, d, K, max_kv_len, kv_tok_stride).total;
+  if (need > ASM_NOALLOC_SCRATCH_BYTES)
+    return fail(ASM_ERR_WORKSPACE,
+                "decode step needs %zu bytes of scratch; asm_decode_step_noalloc holds %zu "
+                "(use asm_decode_step with a workspace)",
+                need, size_t(ASM_NOALLOC_SCRATCH_BYTES));
+  void* ws = nullptr;
+  ASM_TRY(noalloc_scratch(stream, &ws));
+  return decode_impl(dtype, B, Hq, Hkv, d, K, scale, q, C, cinv, Abar, LSEbar, Kl, Vl,
+                     kv_head_stride, kv_tok_stride, kv_capacity, kv_start, kv_len, max_kv_len,
+                     out, out_lse, out_idx, ws, ASM_NOALLOC_SCRATCH_BYTES, stream, nullptr);
 }
 
 // ---------------------------------------------------------------------------

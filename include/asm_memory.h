@@ -25,7 +25,8 @@
  *   - The caller owns every buffer, including the workspace `ws` whose size
  *     the matching *_ws() function returns (0 means ws may be NULL).  The
  *     library allocates no memory and keeps no state between calls except a
- *     thread-local error message.
+ *     thread-local error message and, for asm_decode_step_noalloc only, one
+ *     fixed scratch array per GPU (see there).
  *   - Calls validate their arguments on the host before any launch, enqueue
  *     their kernels on `stream` and return without synchronising.  A
  *     negative status means nothing was enqueued (or, for ASM_ERR_HIP, that
@@ -63,7 +64,7 @@ enum asm_status_code {
 enum asm_dtype { ASM_BF16 = 0, ASM_F32 = 1 };
 
 /* ABI version of this header (bumped on any signature change). */
-#define ASM_ABI_VERSION 6
+#define ASM_ABI_VERSION 7
 int asm_abi_version(void);
 
 /* Static text for a status code. */
@@ -112,6 +113,12 @@ int asm_centroid_inv_norms(int dtype, int H, int K, int d, const void* C, float*
  * A sequence whose kv_len/kv_start is negative, exceeds max_kv_len or runs
  * past kv_capacity is not read: its outputs are NaN (idx still written).
  * kv_len[b] == 0 gives the memory state itself.
+ * Reproducibility: idx is the same on every run.  When the step has more
+ * work units (64 centroids of a head, or 32 local tokens of a kv head) than
+ * the persistent grid has waves, pairs of waves split their units at run
+ * time, so out and out_lse may differ between runs in the last bits (the
+ * local state's grouping changes; see the parity tolerance of the tests).
+ * Smaller steps give one unit per wave and identical results every run.
  */
 size_t asm_decode_step_ws(int dtype, int B, int Hq, int Hkv, int d, int K, int max_kv_len);
 int asm_decode_step(int dtype, int B, int Hq, int Hkv, int d, int K, float scale,
@@ -121,6 +128,37 @@ int asm_decode_step(int dtype, int B, int Hq, int Hkv, int d, int K, float scale
                     const int32_t* kv_start, const int32_t* kv_len, int max_kv_len,
                     float* out, float* out_lse, int32_t* out_idx,
                     void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * asm_decode_step_noalloc -- asm_decode_step without a workspace, for
+ * callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.  The
+ * step's scratch (argmax keys, tile prefix, partial states) lives in one
+ * array of ASM_NOALLOC_SCRATCH_BYTES bytes per GPU, part of the library's
+ * code object: each GPU the library runs on holds it until the process
+ * ends.  The call allocates nothing; the caller still passes every input
+ * and output, with the meaning, layout and results of asm_decode_step.
+ *   - The current HIP device must be the device of `stream`
+ *     (ASM_ERR_SHAPE otherwise).  The first call on a device looks up the
+ *     array's address there (hipGetSymbolAddress, which may load the
+ *     library's device code on that device) and keeps it: make that first
+ *     call outside graph capture; later calls may be captured.
+ *   - A step that needs more scratch than the array holds (what
+ *     asm_decode_step_ws reports for its shape, up to the layout this call
+ *     uses) returns ASM_ERR_WORKSPACE before any launch; asm_decode_step
+ *     with a workspace serves it.
+ *   - Every call on one GPU shares that GPU's array, which keeps the last
+ *     call's contents; nothing in it needs to start at zero.  Calls that
+ *     overlap on one GPU (other streams, other threads, two replays of a
+ *     captured graph in flight) race on it: order them.
+ */
+#define ASM_NOALLOC_SCRATCH_BYTES (16u << 20)
+int asm_decode_step_noalloc(int dtype, int B, int Hq, int Hkv, int d, int K, float scale,
+                            const void* q, const void* C, const float* cinv, const float* Abar,
+                            const float* LSEbar, const void* Kl, const void* Vl,
+                            int64_t kv_head_stride, int64_t kv_tok_stride, int64_t kv_capacity,
+                            const int32_t* kv_start, const int32_t* kv_len, int max_kv_len,
+                            float* out, float* out_lse, int32_t* out_idx, hipStream_t stream);
 
 /*
  * asm_attend_step -- full attention of one decode step, without memory: the

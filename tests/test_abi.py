@@ -41,9 +41,9 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_text():
     L = api.lib()
-    assert L.asm_abi_version() == 6
+    assert L.asm_abi_version() == 7
     text = open(HEADER).read()
-    assert int(re.search(r"#define ASM_ABI_VERSION (\d+)", text).group(1)) == 6
+    assert int(re.search(r"#define ASM_ABI_VERSION (\d+)", text).group(1)) == 7
     assert L.asm_status_str(0) == b"ok"
     assert L.asm_status_str(-5).startswith(b"workspace")
 
@@ -83,6 +83,37 @@ def test_decode_validation_errors_before_any_launch():
     need = L.asm_decode_step_ws(0, 1, 4, 2, 128, 16, 64)
     assert need > 0
     assert _decode(ws=1 << 20, wsb=need - 1) == -5
+
+
+def _decode_noalloc(**over):
+    args = dict(dtype=0, B=1, Hq=4, Hkv=2, d=128, K=16, scale=0.1, q=1 << 20, C=1 << 20,
+                cinv=1 << 20, Abar=1 << 20, LSEbar=1 << 20, Kl=1 << 20, Vl=1 << 20, hs=128 * 64,
+                ts=128, cap=64, ks=1 << 20, kn=1 << 20, m=64, out=1 << 20, lse=NULL, idx=NULL)
+    args.update(over)
+    a = args
+    L = api.lib()
+    return L.asm_decode_step_noalloc(a["dtype"], a["B"], a["Hq"], a["Hkv"], a["d"], a["K"],
+                                     a["scale"], a["q"], a["C"], a["cinv"], a["Abar"], a["LSEbar"],
+                                     a["Kl"], a["Vl"], a["hs"], a["ts"], a["cap"], a["ks"], a["kn"],
+                                     a["m"], a["out"], a["lse"], a["idx"], None)
+
+
+def test_decode_noalloc_validation_and_scratch_limit_before_any_device_call():
+    """The no-allocation decode checks its arguments, then the scratch its
+    shape needs against the fixed per-GPU array, before it touches a device."""
+    L = api.lib()
+    limit = 16 << 20
+    assert re.search(r"#define ASM_NOALLOC_SCRATCH_BYTES \(16u << 20\)", open(HEADER).read())
+    assert _decode_noalloc(dtype=5) == -3
+    assert _decode_noalloc(q=NULL) == -1
+    assert _decode_noalloc(ts=12) == -4
+    # the headline shape fits; 2048 sequences at K=65536 do not
+    assert L.asm_decode_step_ws(0, 32, 32, 8, 128, 8192, 4096) <= limit
+    big = dict(B=2048, Hq=32, Hkv=8, K=65536, m=4096, cap=2048 * 4096, hs=128 * 2048 * 4096)
+    assert L.asm_decode_step_ws(0, 2048, 32, 8, 128, 65536, 4096) > limit
+    assert _decode_noalloc(**big) == -5
+    msg = L.asm_last_error().decode()
+    assert "asm_decode_step_noalloc holds 16777216" in msg and "scratch" in msg
 
 
 def test_workspace_sizes_follow_the_plan():
