@@ -80,7 +80,7 @@ int check_ws(const void* ws, size_t ws_bytes, size_t need) {
 struct DecodePlan {
   bool fast = false;
   int Bc = 0;  // sequences per launch
-  int n_waves = 0, uph = 0, score_uph = 0;      // MFMA path
+  int n_waves = 0, wg_waves = 0, uph = 0, score_uph = 0;  // MFMA path
   int split_tok = 0, S_max = 0, score_tiles = 0;  // VALU path
   size_t off_keys = 0, off_tp = 0, off_pa = 0, off_pl = 0, total = 0;
 };
@@ -125,6 +125,9 @@ DecodePlan plan_decode(int dtype, int B, int Hq, int Hkv, int d, int K, int max_
     if (w < 2) w = 2;
     w = (w + asmk::kMainWaves - 1) / asmk::kMainWaves * asmk::kMainWaves;
     p.n_waves = int(w);
+    // a wave for every unit (whatever the actual lengths, the roles are then
+    // disjoint): smaller workgroups spread the grid over more compute units
+    p.wg_waves = w >= units ? asmk::kSmallWaves : asmk::kMainWaves;
     p.off_keys = off;
     off = asmk::align_up(off + size_t(Hq) * p.Bc * p.uph * sizeof(uint64_t), kAlign);
     p.off_tp = off;
@@ -225,7 +228,7 @@ int decode_impl(int dtype, int B, int Hq, int Hkv, int d, int K, float scale,
   a.kv_head_stride = kv_head_stride; a.kv_tok_stride = kv_tok_stride; a.kv_capacity = kv_capacity;
   a.max_kv_len = max_kv_len;
   a.no_memory = attend_only ? 1 : 0;
-  a.n_waves = p.n_waves; a.uph = p.uph; a.score_uph = p.score_uph;
+  a.n_waves = p.n_waves; a.wg_waves = p.wg_waves; a.uph = p.uph; a.score_uph = p.score_uph;
   a.split_tok = p.split_tok; a.S_max = p.S_max; a.score_tiles = p.score_tiles;
   char* w = static_cast<char*>(ws);
   a.keys = reinterpret_cast<uint64_t*>(w + p.off_keys);

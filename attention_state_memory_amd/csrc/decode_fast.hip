@@ -579,25 +579,28 @@ __device__ __forceinline__ void run_pool(const DecodeArgs& a, const int32_t* tp,
 }  // namespace
 
 // ---------------------------------------------------------------------------
-// One workgroup (block index blk) of the main grid: 8 waves, two per SIMD.
-template <int D, int G>
+// One workgroup (block index blk) of the main grid: NW waves.  Eight (two per
+// SIMD) in general; four when every work unit has a wave of its own, so that
+// the grid covers twice as many compute units (a workgroup's LDS admits one
+// eight-wave workgroup per compute unit).
+template <int D, int G, int NW>
 __device__ __forceinline__ void main_block(const DecodeArgs& a, int blk) {
   __shared__ int32_t tp[kFastMaxBatch + 1];
-  __shared__ int32_t wsum[kMainWaves];
-  __shared__ __attribute__((aligned(16))) char vls[kMainWaves * Tile<D, G>::kVBytes];  // V tile per wave
-  __shared__ int32_t ctr[kMainWaves];  // pool counters: one per pair, or one per wave (disjoint)
+  __shared__ int32_t wsum[NW];
+  __shared__ __attribute__((aligned(16))) char vls[NW * Tile<D, G>::kVBytes];  // V tile per wave
+  __shared__ int32_t ctr[NW];  // pool counters: one per pair, or one per wave (disjoint)
   // the wave index is uniform across the wave; telling the compiler keeps the
   // work-share arithmetic and the buffer resources in scalar registers
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
-  const int64_t gw = int64_t(blk) * kMainWaves + w;
+  const int64_t gw = int64_t(blk) * NW + w;
   const int64_t W = a.n_waves;
   const int64_t SU = int64_t(a.Hq) * a.score_uph;
-  if (threadIdx.x < kMainWaves) ctr[threadIdx.x] = 0;
+  if (threadIdx.x < NW) ctr[threadIdx.x] = 0;
 
   // tiles per kv head of every sequence, exclusive prefix over sequences
   int carry = 0;
-  for (int base = 0; base < a.B; base += kMainThreads) {
+  for (int base = 0; base < a.B; base += (NW * 64)) {
     const int b = base + threadIdx.x;
     const int v = (b < a.B && seq_valid(a, b)) ? (a.kv_len[b] + 31) >> 5 : 0;
     int x = v;
@@ -611,13 +614,13 @@ __device__ __forceinline__ void main_block(const DecodeArgs& a, int blk) {
     int before = carry;
     for (int ww = 0; ww < w; ++ww) before += wsum[ww];
     if (b < a.B) tp[b] = before + x - v;
-    for (int ww = 0; ww < kMainWaves; ++ww) carry += wsum[ww];
+    for (int ww = 0; ww < NW; ++ww) carry += wsum[ww];
     __syncthreads();
   }
   if (threadIdx.x == 0) tp[a.B] = carry;
   __syncthreads();
   if (blk == 0)
-    for (int b = threadIdx.x; b <= a.B; b += kMainThreads) a.tile_prefix[b] = tp[b];
+    for (int b = threadIdx.x; b <= a.B; b += (NW * 64)) a.tile_prefix[b] = tp[b];
   const int64_t U = int64_t(__builtin_amdgcn_readfirstlane(tp[a.B])) * a.Hkv;
 
   // Role of this wave (plan_roles).  Attention pools go to the first Wa
@@ -641,10 +644,10 @@ __device__ __forceinline__ void main_block(const DecodeArgs& a, int blk) {
     }
   } else {
     const int64_t P = W / 2;
-    const int pw = w % (kMainWaves / 2);
-    rank = int64_t(blk) * (kMainWaves / 2) + pw;
+    const int pw = w % (NW / 2);
+    rank = int64_t(blk) * (NW / 2) + pw;
     pool.ctr = &ctr[pw];
-    pool.m = w / (kMainWaves / 2);
+    pool.m = w / (NW / 2);
     pool.su_lo = share_lo(rank, SU, P);
     pool.nsu = share_lo(rank + 1, SU, P) - pool.su_lo;
     const int64_t nt = rank < ro.Wa ? share_lo(rank + 1, U, ro.Wa) - share_lo(rank, U, ro.Wa) : 0;
@@ -654,10 +657,10 @@ __device__ __forceinline__ void main_block(const DecodeArgs& a, int blk) {
   run_pool<D, G>(a, tp, pool, rank, ro.disjoint, int(SU), vl);
 }
 
-template <int D, int G>
-__global__ void __launch_bounds__(kMainThreads) __attribute__((amdgpu_waves_per_eu(2)))
+template <int D, int G, int NW>
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 decode_fast_main(DecodeArgs a) {
-  main_block<D, G>(a, int(blockIdx.x));
+  main_block<D, G, NW>(a, int(blockIdx.x));
 }
 
 // The two-level lookup fused into the main grid: the first lookup_blocks
@@ -666,13 +669,13 @@ decode_fast_main(DecodeArgs a) {
 // data inside the kernel -- the lookup writes the unit keys that the combine
 // reduces -- so at small batch they run side by side instead of one launch
 // after the other.
-template <int D, int G>
-__global__ void __launch_bounds__(kMainThreads) __attribute__((amdgpu_waves_per_eu(2)))
+template <int D, int G, int NW>
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 decode_fast_main_hier(DecodeArgs a, HierArgs h, int lookup_blocks) {
   if (int(blockIdx.x) < lookup_blocks)
-    hier_lookup_block<D>(h, int(blockIdx.x));
+    hier_lookup_block<D, NW * 64>(h, int(blockIdx.x));
   else
-    main_block<D, G>(a, int(blockIdx.x) - lookup_blocks);
+    main_block<D, G, NW>(a, int(blockIdx.x) - lookup_blocks);
 }
 
 // One wave per (b, h): index from the unit keys, gather of the memory
@@ -791,21 +794,32 @@ bool decode_fast_path(int dtype, int d, int G, int K, int64_t kv_tok_stride, int
 template <int D, int G>
 static void launch_fast_hier(const DecodeArgs& a, const HierArgs& h, hipStream_t s) {
   const int lookup_blocks = a.B * a.Hq * h.p;
-  hipLaunchKernelGGL((decode_fast_main_hier<D, G>), dim3(unsigned(lookup_blocks + a.n_waves / kMainWaves)),
-                     dim3(kMainThreads), 0, s, a, h, lookup_blocks);
+  if (a.wg_waves == kSmallWaves)
+    hipLaunchKernelGGL((decode_fast_main_hier<D, G, kSmallWaves>),
+                       dim3(unsigned(lookup_blocks + a.n_waves / kSmallWaves)), dim3(kSmallWaves * 64),
+                       0, s, a, h, lookup_blocks);
+  else
+    hipLaunchKernelGGL((decode_fast_main_hier<D, G, kMainWaves>),
+                       dim3(unsigned(lookup_blocks + a.n_waves / kMainWaves)), dim3(kMainThreads), 0,
+                       s, a, h, lookup_blocks);
   hipLaunchKernelGGL((decode_fast_combine<G>), dim3((a.B * a.Hq + 3) / 4), dim3(256), 0, s, a);
 }
 
 template <int D, int G>
 static void launch_fast(const DecodeArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((decode_fast_main<D, G>), dim3(a.n_waves / kMainWaves), dim3(kMainThreads), 0, s, a);
+  if (a.wg_waves == kSmallWaves)
+    hipLaunchKernelGGL((decode_fast_main<D, G, kSmallWaves>), dim3(a.n_waves / kSmallWaves),
+                       dim3(kSmallWaves * 64), 0, s, a);
+  else
+    hipLaunchKernelGGL((decode_fast_main<D, G, kMainWaves>), dim3(a.n_waves / kMainWaves),
+                       dim3(kMainThreads), 0, s, a);
   hipLaunchKernelGGL((decode_fast_combine<G>), dim3((a.B * a.Hq + 3) / 4), dim3(256), 0, s, a);
 }
 
 template <int D, int G>
 static int occupancy_waves() {
   int blocks = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_fast_main<D, G>, kMainThreads, 0) !=
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_fast_main<D, G, kMainWaves>, kMainThreads, 0) !=
           hipSuccess || blocks < 1)
     blocks = 1;
   return kMainWaves * blocks;

@@ -32,9 +32,9 @@ namespace asmk {
 
 namespace hier {
 
-constexpr int kThreads = 512;  // the workgroup size of the decode main grid
-constexpr int kWaves = kThreads / 64;
-constexpr int kSupersPerThread = (kHierMaxSupers + kThreads - 1) / kThreads;
+// NT: the workgroup size of the decode main grid the lookup runs in
+template <int NT>
+constexpr int supers_per_thread() { return (kHierMaxSupers + NT - 1) / NT; }
 
 // q . row over D bf16 values, the query in LDS as float32
 template <int D>
@@ -53,26 +53,29 @@ __device__ __forceinline__ float dot_row(const uint16_t* row, const float* qs) {
   return acc;
 }
 
-// block-wide maximum of one key per thread (all threads take part)
+// block-wide maximum of one key per thread (all NT threads take part)
+template <int NT>
 __device__ __forceinline__ uint64_t block_max_u64(uint64_t v, uint64_t* red) {
   v = wave_max_u64(v);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();
   uint64_t m = red[0];
 #pragma unroll
-  for (int i = 1; i < kWaves; ++i) m = umax64(m, red[i]);
+  for (int i = 1; i < NT / 64; ++i) m = umax64(m, red[i]);
   __syncthreads();
   return m;
 }
 
 }  // namespace hier
 
-// The lookup of one workgroup (block index blk of the lookup grid).
-template <int D>
+// The lookup of one workgroup of NT threads (block index blk of the lookup
+// grid).
+template <int D, int NT>
 __device__ __forceinline__ void hier_lookup_block(const HierArgs& a, int blk) {
+  constexpr int kSupersPerThread = hier::supers_per_thread<NT>();
   __shared__ float qs[D];
   __shared__ uint64_t keys_s[kHierMaxSupers];
-  __shared__ uint64_t red[hier::kWaves];
+  __shared__ uint64_t red[NT / 64];
   __shared__ int32_t probe_s;
   const int t = threadIdx.x;
   const int r = blk % a.p;        // probe rank of this workgroup
@@ -87,10 +90,10 @@ __device__ __forceinline__ void hier_lookup_block(const HierArgs& a, int blk) {
   const uint16_t* SC = static_cast<const uint16_t*>(a.SC) + size_t(h) * a.S * D;
   const float* scinv = a.scinv + size_t(h) * a.S;
   const int32_t* off = a.offsets + size_t(h) * (a.S + 1);
-  uint64_t sk[hier::kSupersPerThread];
+  uint64_t sk[kSupersPerThread];
 #pragma unroll
-  for (int i = 0; i < hier::kSupersPerThread; ++i) {
-    const int s = t + hier::kThreads * i;
+  for (int i = 0; i < kSupersPerThread; ++i) {
+    const int s = t + NT * i;
     sk[i] = 0ull;
     if (s < a.S && off[s + 1] > off[s])
       sk[i] = argmax_key(hier::dot_row<D>(SC + size_t(s) * D, qs) * scinv[s], uint32_t(s));
@@ -99,7 +102,7 @@ __device__ __forceinline__ void hier_lookup_block(const HierArgs& a, int blk) {
   __syncthreads();
   // rank of each of this thread's supers among the non-empty ones
 #pragma unroll
-  for (int i = 0; i < hier::kSupersPerThread; ++i) {
+  for (int i = 0; i < kSupersPerThread; ++i) {
     if (sk[i] == 0ull) continue;
     int rank = 0;
     for (int s2 = 0; s2 < a.S; ++s2) rank += keys_s[s2] > sk[i] ? 1 : 0;
@@ -114,12 +117,12 @@ __device__ __forceinline__ void hier_lookup_block(const HierArgs& a, int blk) {
     const float* cinv = a.cinv + size_t(h) * a.K;
     const int32_t* mem = a.members + size_t(h) * a.K + off[probe];
     const int n = off[probe + 1] - off[probe];
-    for (int j = t; j < n; j += hier::kThreads) {
+    for (int j = t; j < n; j += NT) {
       const int e = mem[j];
       best = umax64(best, argmax_key(hier::dot_row<D>(C + size_t(e) * D, qs) * cinv[e], uint32_t(e)));
     }
   }
-  best = hier::block_max_u64(best, red);
+  best = hier::block_max_u64<NT>(best, red);
   if (t == 0) {
     a.keys[(size_t(h) * a.B + b) * a.p + r] = best;
     if (a.probes_out != nullptr) a.probes_out[size_t(item) * a.p + r] = probe;

@@ -34,6 +34,8 @@ struct DecodeArgs {
   int32_t* out_idx;
   // MFMA path
   int n_waves;           // persistent waves (multiple of kMainWaves)
+  int wg_waves;          // waves per workgroup of the main launch: kMainWaves, or
+                         // kSmallWaves when every work unit has a wave of its own
   int uph;               // argmax keys per (head, sequence): ceil(K / 64) units
   int score_uph;         // units per head the main kernel scores: uph, or 0 when
                          // the keys were written beforehand (hierarchical lookup)
@@ -52,6 +54,7 @@ struct DecodeArgs {
 constexpr int kFastMaxBatch = 2048;  // sequences per MFMA-path launch
 constexpr int kMainWaves = 8;        // waves per workgroup of the MFMA main grid (two per SIMD)
 constexpr int kMainThreads = 64 * kMainWaves;
+constexpr int kSmallWaves = 4;       // waves per workgroup when the grid has a wave per work unit
 bool decode_fast_path(int dtype, int d, int G, int K, int64_t kv_tok_stride, int max_kv_len);
 int decode_fast_waves_per_cu(int d, int G);  // resident waves per CU of the MFMA main kernel
 hipError_t launch_decode_fast(const DecodeArgs& a, hipStream_t s);
