@@ -438,11 +438,23 @@ __device__ __forceinline__ void consume_tile(const Tile<D, G>& t, Running<D, G>&
 
 // Segment (sequence b, kv head g) holding global tile x, from the tile
 // prefix in LDS; x0 is the segment's first global tile, nt its tile count.
+// n and st0 are the sequence's local length and first token slot, from the
+// copies in LDS that the block took while scanning the lengths (a global load
+// there would put a memory round trip in front of the segment's first tile).
 struct SegLoc {
   int b, g, nt;
   int64_t x0;
+  int n, st0;
 };
-__device__ __forceinline__ SegLoc locate(const DecodeArgs& a, const int32_t* tp, int64_t x) {
+// The sequences as the workgroup sees them, in LDS: tile prefix [B + 1],
+// local lengths and first slots [B].
+struct SeqTab {
+  const int32_t* tp;
+  const int32_t* len;
+  const int32_t* st;
+};
+__device__ __forceinline__ SegLoc locate(const DecodeArgs& a, const SeqTab& S, int64_t x) {
+  const int32_t* tp = S.tp;
   // LDS reads land in vector registers; readfirstlane marks the (wave-
   // uniform) values as scalars so the buffer resources built from them stay
   // in SGPRs (otherwise every buffer load becomes a waterfall loop).
@@ -454,7 +466,8 @@ __device__ __forceinline__ SegLoc locate(const DecodeArgs& a, const int32_t* tp,
   const int tb0 = __builtin_amdgcn_readfirstlane(tp[blo]);
   const int nt = __builtin_amdgcn_readfirstlane(tp[blo + 1]) - tb0;
   const int g = int((x - int64_t(tb0) * a.Hkv) / nt);
-  return {blo, g, nt, int64_t(tb0) * a.Hkv + int64_t(g) * nt};
+  return {blo, g, nt, int64_t(tb0) * a.Hkv + int64_t(g) * nt,
+          __builtin_amdgcn_readfirstlane(S.len[blo]), __builtin_amdgcn_readfirstlane(S.st[blo])};
 }
 
 // Attends the tiles of segment L that this wave claims, starting with the
@@ -472,8 +485,8 @@ __device__ __forceinline__ int64_t attn_run(const DecodeArgs& a, const SegLoc& L
   const int lane = threadIdx.x & 63;
   const int r16 = lane & 15, grp = lane >> 4;
   const int b = L.b, g = L.g;
-  const int n = __builtin_amdgcn_readfirstlane(a.kv_len[b]);
-  const int64_t st0 = __builtin_amdgcn_readfirstlane(a.kv_start[b]);
+  const int n = L.n;
+  const int64_t st0 = L.st0;
   const int64_t ts = a.kv_tok_stride;
   const uint32_t seg_bytes = uint32_t(n) * uint32_t(ts) * 2u;
   const char* kseg = uniform_ptr(reinterpret_cast<const char*>(static_cast<const uint16_t*>(a.Kl) + g * a.kv_head_stride + st0 * ts));
@@ -550,7 +563,7 @@ __device__ __forceinline__ int64_t attn_run(const DecodeArgs& a, const SegLoc& L
 // run contiguously from its end of the pool, so the segments it attends
 // form one range.
 template <int D, int G>
-__device__ __forceinline__ void run_pool(const DecodeArgs& a, const int32_t* tp, PairPool& pool,
+__device__ __forceinline__ void run_pool(const DecodeArgs& a, const SeqTab& S, PairPool& pool,
                                          int64_t r, bool disjoint, int SU, char* vlds) {
   int64_t s_lo = -1, s_hi = -2;  // segments attended
   int64_t v = claim(pool);
@@ -560,14 +573,14 @@ __device__ __forceinline__ void run_pool(const DecodeArgs& a, const int32_t* tp,
       continue;
     }
     const int64_t x = pool_tile(pool, v);
-    const SegLoc L = locate(a, tp, x);
+    const SegLoc L = locate(a, S, x);
     const int64_t seg = int64_t(L.b) * a.Hkv + L.g;
     s_lo = s_lo < 0 ? seg : min(s_lo, seg);
     s_hi = max(s_hi, seg);
     v = attn_run<D, G>(a, L, x, pool, piece_slot(disjoint, r, seg, pool.m), vlds);
   }
   if (pool.n > pool.nsu) {
-    const SegLoc F = locate(a, tp, pool.t_lo), E = locate(a, tp, pool.t_lo + (pool.n - pool.nsu) - 1);
+    const SegLoc F = locate(a, S, pool.t_lo), E = locate(a, S, pool.t_lo + (pool.n - pool.nsu) - 1);
     const int64_t f = int64_t(F.b) * a.Hkv + F.g, e = int64_t(E.b) * a.Hkv + E.g;
     const int lane = threadIdx.x & 63;
     for (int64_t seg = f; seg <= e; ++seg)
@@ -586,6 +599,7 @@ __device__ __forceinline__ void run_pool(const DecodeArgs& a, const int32_t* tp,
 template <int D, int G, int NW>
 __device__ __forceinline__ void main_block(const DecodeArgs& a, int blk) {
   __shared__ int32_t tp[kFastMaxBatch + 1];
+  __shared__ int32_t sq_len[kFastMaxBatch], sq_st[kFastMaxBatch];
   __shared__ int32_t wsum[NW];
   __shared__ __attribute__((aligned(16))) char vls[NW * Tile<D, G>::kVBytes];  // V tile per wave
   __shared__ int32_t ctr[NW];  // pool counters: one per pair, or one per wave (disjoint)
@@ -602,7 +616,14 @@ __device__ __forceinline__ void main_block(const DecodeArgs& a, int blk) {
   int carry = 0;
   for (int base = 0; base < a.B; base += (NW * 64)) {
     const int b = base + threadIdx.x;
-    const int v = (b < a.B && seq_valid(a, b)) ? (a.kv_len[b] + 31) >> 5 : 0;
+    int v = 0;
+    if (b < a.B) {
+      const int n = a.kv_len[b], st = a.kv_start[b];
+      sq_len[b] = n;
+      sq_st[b] = st;
+      const bool valid = n >= 0 && n <= a.max_kv_len && st >= 0 && int64_t(st) + n <= a.kv_capacity;
+      v = valid ? (n + 31) >> 5 : 0;
+    }
     int x = v;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -654,7 +675,7 @@ __device__ __forceinline__ void main_block(const DecodeArgs& a, int blk) {
     pool.t_lo = rank < ro.Wa ? share_lo(rank, U, ro.Wa) : 0;
     pool.n = pool.nsu + nt;
   }
-  run_pool<D, G>(a, tp, pool, rank, ro.disjoint, int(SU), vl);
+  run_pool<D, G>(a, SeqTab{tp, sq_len, sq_st}, pool, rank, ro.disjoint, int(SU), vl);
 }
 
 template <int D, int G, int NW>
