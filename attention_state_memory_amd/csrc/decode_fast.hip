@@ -702,9 +702,9 @@ decode_fast_main_hier(DecodeArgs a, HierArgs h, int lookup_blocks) {
 // One wave per (b, h): index from the unit keys, gather of the memory
 // state, merge with the partial states of segment (b, h / G).  The loads are
 // arranged in two dependent rounds: (1) sequence bounds, tile prefix, keys;
-// (2) the gathered memory state, the piece normalisers and the first 16
-// piece rows (rows past the last piece read as zeros through the buffer
-// bounds); later pieces, if any, follow 16 rows at a time.
+// (2) the gathered memory state, the piece normalisers and up to 64 piece
+// rows (rows past the last piece read as zeros through the buffer bounds);
+// later pieces, if any, follow 16 rows at a time.
 template <int G>
 __global__ void __launch_bounds__(256) decode_fast_combine(DecodeArgs a) {
   const int lane = threadIdx.x & 63;
@@ -751,14 +751,21 @@ __global__ void __launch_bounds__(256) decode_fast_combine(DecodeArgs a) {
                         : make_float2(0.f, 0.f);
   const float* pa0 = a.part_a + (p0 * G + hh) * D;
   const auto rp = make_rsrc(pa0, np > 0 ? uint32_t(((np - 1) * G + 1) * D * 4) : 0u);
-  // the first 64 piece normalisers and the first 16 piece rows load with the
-  // memory state (rows past the last piece read as zeros)
+  // the first 64 piece normalisers and piece rows load with the memory state,
+  // in groups of 16 rows as far as the segment has pieces (rows past the
+  // last piece read as zeros); a segment split over many waves (a long
+  // context at small batch) thus merges its first 64 pieces after one round
   const float lc0 = lane < np ? a.part_lse[(p0 + lane) * G + hh] : -INFINITY;
-  u32x2 r0[16];
+  u32x2 r0[64];
 #pragma unroll
-  for (int i = 0; i < 16; ++i)
-    r0[i] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
-                                          rp, int((i * G * D + dd) * 4), 0, 0));
+  for (int j = 0; j < 4; ++j) {
+    if (np > 16 * j) {
+#pragma unroll
+      for (int i = 16 * j; i < 16 * j + 16; ++i)
+        r0[i] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                                              rp, int((i * G * D + dd) * 4), 0, 0));
+    }
+  }
   float M = fmaxf(lm, lc0);
   for (int64_t c = 64 + lane; c < np; c += 64) M = fmaxf(M, a.part_lse[(p0 + c) * G + hh]);
 #pragma unroll
@@ -770,31 +777,33 @@ __global__ void __launch_bounds__(256) decode_fast_combine(DecodeArgs a) {
   }
   const float wm = lm == -INFINITY ? 0.0f : expf(lm - M);
   float v0 = wm > 0.0f ? wm * am.x : 0.0f, v1 = wm > 0.0f ? wm * am.y : 0.0f;
-  float zsum = 0.0f;
-  for (int64_t c64 = 0; c64 < np; c64 += 64) {
-    const float lc = c64 == 0 ? lc0
-                   : (c64 + lane < np ? a.part_lse[(p0 + c64 + lane) * G + hh] : -INFINITY);
+  // an empty piece (weight 0) may hold stale values: skip it
+  const auto acc = [&](float wi, const u32x2& r) {
+    v0 = wi > 0.0f ? fmaf(wi, __uint_as_float(r[0]), v0) : v0;
+    v1 = wi > 0.0f ? fmaf(wi, __uint_as_float(r[1]), v1) : v1;
+  };
+  const float wc0 = lc0 == -INFINITY ? 0.0f : expf(lc0 - M);
+  float zsum = wc0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (np > 16 * j) {
+#pragma unroll
+      for (int i = 16 * j; i < 16 * j + 16; ++i) acc(readlane_f(wc0, i), r0[i]);
+    }
+  }
+  for (int64_t c64 = 64; c64 < np; c64 += 64) {
+    const float lc = c64 + lane < np ? a.part_lse[(p0 + c64 + lane) * G + hh] : -INFINITY;
     const float wc = lc == -INFINITY ? 0.0f : expf(lc - M);
     zsum += wc;
     const int64_t cend = min<int64_t>(np, c64 + 64);
     for (int64_t c = c64; c < cend; c += 16) {
       u32x2 r[16];
-      if (c == 0) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) r[i] = r0[i];
-      } else {
+      for (int i = 0; i < 16; ++i)
+        r[i] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                                             rp, int(((c + i) * G * D + dd) * 4), 0, 0));
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-          r[i] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
-                                               rp, int(((c + i) * G * D + dd) * 4), 0, 0));
-      }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        // an empty piece (weight 0) may hold stale values: skip it
-        const float wi = readlane_f(wc, int(c - c64) + i);
-        v0 = wi > 0.0f ? fmaf(wi, __uint_as_float(r[i][0]), v0) : v0;
-        v1 = wi > 0.0f ? fmaf(wi, __uint_as_float(r[i][1]), v1) : v1;
-      }
+      for (int i = 0; i < 16; ++i) acc(readlane_f(wc, int(c - c64) + i), r[i]);
     }
   }
   const float Z = wm + wave_sum(zsum);
