@@ -99,8 +99,11 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="wall-clock budget of the CPU oracle baseline (0 disables it)")
     p.add_argument("--copy-calibration", action="store_true",
-                   help="run one plain device copy (256 MiB read, 256 MiB written) before the "
-                        "timed region, as the reference kernel for HBM byte counters")
+                   help="run one plain device copy (256 MiB read, 256 MiB written) before any "
+                        "workload, as the reference kernel for HBM byte counters")
+    p.add_argument("--queries", type=int, default=4096,
+                   help="prefix_states / prefix_states_streamed: calibration queries per head "
+                        "(65536 is the memory-build scale)")
     p.add_argument("--K", type=int, default=8192, help="layer_decode_hier: entries per head")
     p.add_argument("--supers", type=int, default=128, help="layer_decode_hier: super-centroids S")
     p.add_argument("--probes", type=int, default=8, help="layer_decode_hier: probes p")
@@ -120,6 +123,10 @@ def main():
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; "
                                    "no multi-GPU mode"}))
         sys.exit(2)
+    if args.copy_calibration:
+        import torch
+        torch.cuda.set_device(torch.device("cuda:0"))
+        copy_calibration(torch, torch.device("cuda:0"))
     if args.workload == "layer_decode":
         run_layers(args)
         return
@@ -146,8 +153,6 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    if args.copy_calibration:
-        copy_calibration(torch, dev)
 
     def to_dev(x):
         x = np.ascontiguousarray(x)
@@ -778,7 +783,7 @@ def run_build(args):
         return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
 
     if args.workload == "prefix_states":
-        w = synth.prefix_states()
+        w = synth.prefix_states(N=args.queries)
         Q, Kp, Vp = to_dev(w["Q"]), to_dev(w["Kp"]), to_dev(w["Vp"])
         Hq, N, L, d, chunk = w["Hq"], w["N"], w["L"], w["d"], w["chunk"]
         nc = -(-L // chunk)
@@ -828,7 +833,7 @@ def run_build(args):
         return
 
     if args.workload == "prefix_states_streamed":
-        run_streamed(args, w=synth.prefix_states(), to_dev=to_dev)
+        run_streamed(args, w=synth.prefix_states(N=args.queries), to_dev=to_dev)
         return
 
     # memory_build: states over the prefix, 10 Lloyd iterations, aggregation
