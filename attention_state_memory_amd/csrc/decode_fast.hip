@@ -48,20 +48,35 @@ __device__ __forceinline__ int64_t share_lo(int64_t w, int64_t total, int64_t W)
 //   disjoint  the grid has a wave for every unit (small, latency-bound
 //             steps): one unit per wave, attention tiles on waves [0, U),
 //             scoring units on waves [W - SU, W); ranks are waves;
-//   otherwise every wave pair p < P = W / 2 gets the same mix: scoring units
+//   mixed     (at least 4 tiles per pair) every wave pair p < P = W / 2 gets
+//             the same mix: scoring units
 //             [p SU / P, (p+1) SU / P) and, for the first Wa = min(P, U)
 //             pairs, tiles [p U / Wa, (p+1) U / Wa).  The memory system
 //             serves every compute unit about equally, so equal bytes per
 //             pair (four pairs per compute unit) make the waves finish
 //             together.  Ranks are pairs.
+//   scarce    (fewer than 4 tiles per pair) the tiles and then the scoring
+//             units, as one sequence of SU + U items, cut into P equal
+//             contiguous ranges, one per pair, so that the tiles sit on
+//             fewer pairs (a segment's partial states stay few) while every
+//             pair still gets the same work.
+// Tile x lives at rank wave_of(x, tot, Wt).
 struct Roles {
-  int64_t Wa;  // ranks that hold tiles
+  int64_t Wa;       // ranks that hold tiles
   bool disjoint;
+  bool scarce;      // the contiguous layout for few tiles
+  int64_t tot, Wt;  // tile x -> rank wave_of(x, tot, Wt)
 };
 __device__ __forceinline__ Roles plan_roles(const DecodeArgs& a, int64_t W, int64_t U) {
   const int64_t SU = int64_t(a.Hq) * a.score_uph;
-  if (SU + U <= W) return {U, true};
-  return {min(W / 2, U), false};
+  if (SU + U <= W) return {U, true, false, U, U};
+  const int64_t P = W / 2;
+  if (U < 4 * P) {
+    const int64_t T = SU + U;
+    return {U > 0 ? ((U * P - 1) / T) + 1 : 0, false, true, T, P};
+  }
+  const int64_t Wa = min(P, U);
+  return {Wa, false, false, U, Wa};
 }
 // Partial-state slot of rank r's piece of segment seg: one per rank
 // (disjoint) or one per wave of the pair (member m).  The slots of one
@@ -669,10 +684,19 @@ __device__ __forceinline__ void main_block(const DecodeArgs& a, int blk) {
     rank = int64_t(blk) * (NW / 2) + pw;
     pool.ctr = &ctr[pw];
     pool.m = w / (NW / 2);
-    pool.su_lo = share_lo(rank, SU, P);
-    pool.nsu = share_lo(rank + 1, SU, P) - pool.su_lo;
-    const int64_t nt = rank < ro.Wa ? share_lo(rank + 1, U, ro.Wa) - share_lo(rank, U, ro.Wa) : 0;
-    pool.t_lo = rank < ro.Wa ? share_lo(rank, U, ro.Wa) : 0;
+    int64_t nt;
+    if (ro.scarce) {
+      const int64_t lo = share_lo(rank, ro.tot, P), hi = share_lo(rank + 1, ro.tot, P);
+      pool.t_lo = min(lo, U);
+      nt = min(hi, U) - pool.t_lo;
+      pool.su_lo = max(lo, U) - U;
+      pool.nsu = max(hi, U) - max(lo, U);
+    } else {
+      pool.su_lo = share_lo(rank, SU, P);
+      pool.nsu = share_lo(rank + 1, SU, P) - pool.su_lo;
+      nt = rank < ro.Wa ? share_lo(rank + 1, U, ro.Wa) - share_lo(rank, U, ro.Wa) : 0;
+      pool.t_lo = rank < ro.Wa ? share_lo(rank, U, ro.Wa) : 0;
+    }
     pool.n = pool.nsu + nt;
   }
   run_pool<D, G>(a, SeqTab{tp, sq_len, sq_st}, pool, rank, ro.disjoint, int(SU), vl);
@@ -730,7 +754,7 @@ __global__ void __launch_bounds__(256) decode_fast_combine(DecodeArgs a) {
     const Roles ro = plan_roles(a, a.n_waves, total);
     const int64_t first = int64_t(tpb) * a.Hkv + int64_t(g) * nt;
     const int64_t seg = int64_t(b) * a.Hkv + g;
-    const int64_t r0 = wave_of(first, total, ro.Wa), r1 = wave_of(first + nt - 1, total, ro.Wa);
+    const int64_t r0 = wave_of(first, ro.tot, ro.Wt), r1 = wave_of(first + nt - 1, ro.tot, ro.Wt);
     p0 = piece_slot(ro.disjoint, r0, seg, 0);
     np = (ro.disjoint ? 1 : 2) * (r1 - r0 + 1);
   }
