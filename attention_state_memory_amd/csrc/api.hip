@@ -110,15 +110,20 @@ DecodePlan plan_decode(int dtype, int B, int Hq, int Hkv, int d, int K, int max_
   DecodePlan p;
   const int G = Hq / Hkv;
   p.fast = asmk::decode_fast_path(dtype, d, G, K, kv_tok_stride, max_kv_len);
+  const int Bc = B < asmk::kFastMaxBatch ? B : asmk::kFastMaxBatch;
+  const int uph = keys_given > 0 ? keys_given : (K + 63) / 64;
+  const int score_uph = keys_given > 0 ? 0 : uph;
+  const int64_t units = int64_t(Hq) * score_uph + int64_t(Bc) * Hkv * ((int64_t(max_kv_len) + 31) / 32);
+  // the pools count their claims and index scoring halves in 32 bits
+  if (units >= (int64_t(1) << 30)) p.fast = false;
   size_t off = 0;
   if (p.fast) {
-    p.Bc = B < asmk::kFastMaxBatch ? B : asmk::kFastMaxBatch;
-    p.uph = keys_given > 0 ? keys_given : (K + 63) / 64;
-    p.score_uph = keys_given > 0 ? 0 : p.uph;
+    p.Bc = Bc;
+    p.uph = uph;
+    p.score_uph = score_uph;
     // Persistent grid: as many waves as fit on the device at once, but no
     // more than one per work unit (16 KB each): small steps are latency-bound
     // and gain from spreading their few units over many waves.
-    const int64_t units = int64_t(Hq) * p.score_uph + int64_t(p.Bc) * Hkv * ((int64_t(max_kv_len) + 31) / 32);
     const int64_t cap = int64_t(device_cus()) * asmk::decode_fast_waves_per_cu(d, G);
     int64_t w = units;
     w = w < cap ? w : cap;
@@ -212,12 +217,12 @@ int decode_impl(int dtype, int B, int Hq, int Hkv, int d, int K, float scale,
                                    hier != nullptr ? hier->p : (attend_only ? 1 : 0));
   if (attend_only && !p.fast)
     return fail(ASM_ERR_SHAPE,
-                "attention without memory needs bf16, d in {64, 128}, Hq/Hkv in {1, 2, 4, 8} "
-                "and KV rows of under 2 GiB per sequence");
+                "attention without memory needs bf16, d in {64, 128}, Hq/Hkv in {1, 2, 4, 8}, "
+                "KV rows of under 2 GiB per sequence and under 2^30 work units per launch");
   if (hier != nullptr && !p.fast)
     return fail(ASM_ERR_SHAPE,
-                "the hierarchical lookup needs bf16, d in {64, 128}, Hq/Hkv in {1, 2, 4, 8} "
-                "and local KV rows of under 2 GiB per sequence");
+                "the hierarchical lookup needs bf16, d in {64, 128}, Hq/Hkv in {1, 2, 4, 8}, "
+                "local KV rows of under 2 GiB per sequence and under 2^30 work units per launch");
   ASM_TRY(check_ws(ws, ws_bytes, p.total));
 
   asmk::DecodeArgs a{};

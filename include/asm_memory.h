@@ -172,8 +172,9 @@ int asm_decode_step_noalloc(int dtype, int B, int Hq, int Hkv, int d, int K, flo
  * It runs the split-K attention and merge of asm_decode_step with the lookup
  * switched off and the merge started from the empty state.  Arguments as
  * asm_decode_step (Kc, Vc take the place of Kl, Vl); kv_len[b] == 0 gives
- * (0, -inf).  Needs bf16, d in {64, 128}, Hq/Hkv in {1, 2, 4, 8} and each
- * sequence's rows within 2 GiB; otherwise ASM_ERR_SHAPE (and _ws returns 0).
+ * (0, -inf).  Needs bf16, d in {64, 128}, Hq/Hkv in {1, 2, 4, 8}, each
+ * sequence's rows within 2 GiB and min(B, 2048) * Hkv * ceil(max_kv_len / 32)
+ * below 2^30; otherwise ASM_ERR_SHAPE (and _ws returns 0).
  */
 size_t asm_attend_step_ws(int dtype, int B, int Hq, int Hkv, int d, int max_kv_len);
 int asm_attend_step(int dtype, int B, int Hq, int Hkv, int d, float scale, const void* q,

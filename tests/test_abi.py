@@ -140,6 +140,18 @@ def test_decode_table_too_large_for_32_bit_offsets_takes_the_generic_path():
         ((k_big - 1 + 255) // 256) * 8 + 512 + 256
 
 
+def test_step_over_2_30_work_units_leaves_the_mfma_path():
+    """The MFMA path counts pool claims and scoring halves in 32 bits, so its
+    planner takes at most 2^30 work units (32-token tiles plus 64-entry
+    scoring units) per launch: attention without memory has no other path
+    (workspace 0, ASM_ERR_SHAPE), the decode falls back to the generic path."""
+    L = api.lib()
+    d, Hkv = 128, 8
+    fits = (1 << 21) - 32  # 2048 * 8 * ceil(fits / 32) < 2^30
+    assert L.asm_attend_step_ws(0, 2048, 8, Hkv, d, fits) > 0
+    assert L.asm_attend_step_ws(0, 2048, 8, Hkv, d, 1 << 21) == 0
+
+
 def test_build_assign_aggregate_validation():
     L = api.lib()
     st = L.asm_build_states(0, 4, 3, 8, 16, 128, 4, 0.1, 1 << 20, 1 << 20, 1 << 20, None, None,
