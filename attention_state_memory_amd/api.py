@@ -33,6 +33,14 @@ SIGNATURES = {
                                  _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                  _c_i64, _c_i64, _c_i64, _vp, _vp, _c_int,
                                  _vp, _vp, _vp, _vp, _c_size, _vp]),
+    "asm_decode_step_begin": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_float,
+                                       _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                       _c_i64, _c_i64, _c_i64, _vp, _vp, _c_int,
+                                       _vp, _vp, _vp, _vp, _c_size, _vp]),
+    "asm_decode_step_finish": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_float,
+                                        _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                        _c_i64, _c_i64, _c_i64, _vp, _vp, _c_int,
+                                        _vp, _vp, _vp, _vp, _c_size, _vp]),
     "asm_decode_step_noalloc": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_float,
                                          _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                          _c_i64, _c_i64, _c_i64, _vp, _vp, _c_int,
@@ -209,6 +217,45 @@ def decode_step(q, C, cinv, Abar, LSEbar, Kl, Vl, kv_start, kv_len, max_kv_len: 
         _ptr(kv_start), _ptr(kv_len), int(max_kv_len), _ptr(out), _ptr(out_lse), _ptr(out_idx),
         _ptr(ws), nbytes, _stream(dev)))
     return out, out_lse, out_idx
+
+
+def _decode_phase(name, q, C, cinv, Abar, LSEbar, Kl, Vl, kv_start, kv_len, max_kv_len, scale,
+                  out, out_lse, out_idx, workspace):
+    code = _decode_operands(q, C, cinv, Abar, LSEbar, Kl, Vl, kv_start, kv_len)
+    B, Hq, d = q.shape
+    K = C.shape[1]
+    Hkv, cap, _ = Kl.shape
+    _dev(out, "out", torch.float32)
+    for t, n, dt in ((out_lse, "out_lse", torch.float32), (out_idx, "out_idx", torch.int32)):
+        if t is not None:
+            _dev(t, n, dt)
+    _dev(workspace, "workspace")
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(name, getattr(lib(), name)(
+        code, B, Hq, Hkv, d, K, float(scale), _ptr(q), _ptr(C), _ptr(cinv), _ptr(Abar),
+        _ptr(LSEbar), _ptr(Kl), _ptr(Vl), Kl.stride(0), Kl.stride(1), cap,
+        _ptr(kv_start), _ptr(kv_len), int(max_kv_len), _ptr(out), _ptr(out_lse), _ptr(out_idx),
+        _ptr(workspace), nbytes, _stream(q.device)))
+    return out, out_lse, out_idx
+
+
+def decode_step_begin(q, C, cinv, Abar, LSEbar, Kl, Vl, kv_start, kv_len, max_kv_len: int,
+                      scale: float, *, out, out_lse=None, out_idx=None, workspace):
+    """First launch of decode_step (scoring and local attention into the
+    workspace).  decode_step_finish with the same arguments and workspace,
+    on the same stream, completes the step.  The workspace is required
+    (decode_step_ws bytes) and shared by the two calls."""
+    return _decode_phase("asm_decode_step_begin", q, C, cinv, Abar, LSEbar, Kl, Vl, kv_start,
+                         kv_len, max_kv_len, scale, out, out_lse, out_idx, workspace)
+
+
+def decode_step_finish(q, C, cinv, Abar, LSEbar, Kl, Vl, kv_start, kv_len, max_kv_len: int,
+                       scale: float, *, out, out_lse=None, out_idx=None, workspace):
+    """Second launch of decode_step (index, gather and merge into out,
+    out_lse, out_idx), after decode_step_begin with the same arguments and
+    workspace.  Returns (out, out_lse, out_idx)."""
+    return _decode_phase("asm_decode_step_finish", q, C, cinv, Abar, LSEbar, Kl, Vl, kv_start,
+                         kv_len, max_kv_len, scale, out, out_lse, out_idx, workspace)
 
 
 def decode_step_noalloc(q, C, cinv, Abar, LSEbar, Kl, Vl, kv_start, kv_len, max_kv_len: int,

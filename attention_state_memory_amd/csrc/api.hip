@@ -201,7 +201,9 @@ int check_decode_args(int dtype, int B, int Hq, int Hkv, int d, int K, float sca
 
 // The decode step for every lookup; `hier` (hierarchical lookup) is NULL for
 // the flat search; `qs` (the queries the lookup scores) is NULL when they are
-// the queries themselves.
+// the queries themselves.  `phase`: 3 the whole step; 1 its first launch
+// (the main grid), 2 its second (the merge), for the flat MFMA path in one
+// launch.
 int decode_impl(int dtype, int B, int Hq, int Hkv, int d, int K, float scale,
                 const void* q, const void* C, const float* cinv, const float* Abar,
                 const float* LSEbar, const void* Kl, const void* Vl,
@@ -209,7 +211,7 @@ int decode_impl(int dtype, int B, int Hq, int Hkv, int d, int K, float scale,
                 const int32_t* kv_start, const int32_t* kv_len, int max_kv_len,
                 float* out, float* out_lse, int32_t* out_idx,
                 void* ws, size_t ws_bytes, hipStream_t stream, asmk::HierArgs* hier,
-                const void* qs = nullptr, bool attend_only = false) {
+                const void* qs = nullptr, bool attend_only = false, int phase = 3) {
   ASM_TRY(check_decode_args(dtype, B, Hq, Hkv, d, K, scale, q, C, cinv, Abar, LSEbar, Kl, Vl,
                             kv_head_stride, kv_tok_stride, kv_capacity, kv_start, kv_len,
                             max_kv_len, out, attend_only));
@@ -223,6 +225,11 @@ int decode_impl(int dtype, int B, int Hq, int Hkv, int d, int K, float scale,
     return fail(ASM_ERR_SHAPE,
                 "the hierarchical lookup needs bf16, d in {64, 128}, Hq/Hkv in {1, 2, 4, 8}, "
                 "local KV rows of under 2 GiB per sequence and under 2^30 work units per launch");
+  if (phase != 3 && (!p.fast || hier != nullptr || attend_only || B > p.Bc))
+    return fail(ASM_ERR_SHAPE,
+                "the decode in two launches needs bf16, d in {64, 128}, Hq/Hkv in {1, 2, 4, 8}, "
+                "KV rows of under 2 GiB per sequence and at most %d sequences",
+                asmk::kFastMaxBatch);
   ASM_TRY(check_ws(ws, ws_bytes, p.total));
 
   asmk::DecodeArgs a{};
@@ -263,7 +270,10 @@ int decode_impl(int dtype, int B, int Hq, int Hkv, int d, int K, float scale,
       if (sth != ASM_OK) return sth;
       continue;
     }
-    const int st = hip_status(asmk::launch_decode(a, dtype, stream), "decode_step");
+    const hipError_t e = phase == 1   ? asmk::launch_decode_fast_main(a, stream)
+                         : phase == 2 ? asmk::launch_decode_fast_merge(a, stream)
+                                      : asmk::launch_decode(a, dtype, stream);
+    const int st = hip_status(e, "decode_step");
     if (st != ASM_OK) return st;
   }
   return ASM_OK;
@@ -367,6 +377,30 @@ int asm_decode_step(int dtype, int B, int Hq, int Hkv, int d, int K, float scale
   return decode_impl(dtype, B, Hq, Hkv, d, K, scale, q, C, cinv, Abar, LSEbar, Kl, Vl,
                      kv_head_stride, kv_tok_stride, kv_capacity, kv_start, kv_len, max_kv_len,
                      out, out_lse, out_idx, ws, ws_bytes, stream, nullptr);
+}
+
+int asm_decode_step_begin(int dtype, int B, int Hq, int Hkv, int d, int K, float scale,
+                          const void* q, const void* C, const float* cinv, const float* Abar,
+                          const float* LSEbar, const void* Kl, const void* Vl,
+                          int64_t kv_head_stride, int64_t kv_tok_stride, int64_t kv_capacity,
+                          const int32_t* kv_start, const int32_t* kv_len, int max_kv_len,
+                          float* out, float* out_lse, int32_t* out_idx,
+                          void* ws, size_t ws_bytes, hipStream_t stream) {
+  return decode_impl(dtype, B, Hq, Hkv, d, K, scale, q, C, cinv, Abar, LSEbar, Kl, Vl,
+                     kv_head_stride, kv_tok_stride, kv_capacity, kv_start, kv_len, max_kv_len,
+                     out, out_lse, out_idx, ws, ws_bytes, stream, nullptr, nullptr, false, 1);
+}
+
+int asm_decode_step_finish(int dtype, int B, int Hq, int Hkv, int d, int K, float scale,
+                           const void* q, const void* C, const float* cinv, const float* Abar,
+                           const float* LSEbar, const void* Kl, const void* Vl,
+                           int64_t kv_head_stride, int64_t kv_tok_stride, int64_t kv_capacity,
+                           const int32_t* kv_start, const int32_t* kv_len, int max_kv_len,
+                           float* out, float* out_lse, int32_t* out_idx,
+                           void* ws, size_t ws_bytes, hipStream_t stream) {
+  return decode_impl(dtype, B, Hq, Hkv, d, K, scale, q, C, cinv, Abar, LSEbar, Kl, Vl,
+                     kv_head_stride, kv_tok_stride, kv_capacity, kv_start, kv_len, max_kv_len,
+                     out, out_lse, out_idx, ws, ws_bytes, stream, nullptr, nullptr, false, 2);
 }
 
 // ---------------------------------------------------------------------------

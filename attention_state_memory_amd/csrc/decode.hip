@@ -162,7 +162,8 @@ __global__ void __launch_bounds__(256) attn_generic(DecodeArgs a) {
 // host side
 // ---------------------------------------------------------------------------
 hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t s) {
-  if (decode_fast_path(dtype, a.d, a.Hq / a.Hkv, a.K, a.kv_tok_stride, a.max_kv_len)) return launch_decode_fast(a, s);
+  // the planner chose the path (and sized the workspace for it)
+  if (a.n_waves > 0) return launch_decode_fast(a, s);
   const int n_attn = a.B * a.Hkv * a.S_max;
   if (dtype == 1) {
     hipLaunchKernelGGL(score_generic<float>, dim3(a.score_tiles, a.Hq), dim3(256), 0, s, a);

@@ -859,15 +859,19 @@ static void launch_fast_hier(const DecodeArgs& a, const HierArgs& h, hipStream_t
   hipLaunchKernelGGL((decode_fast_combine<G>), dim3((a.B * a.Hq + 3) / 4), dim3(256), 0, s, a);
 }
 
+// phase bit 1: the main grid; bit 2: the merge
 template <int D, int G>
-static void launch_fast(const DecodeArgs& a, hipStream_t s) {
-  if (a.wg_waves == kSmallWaves)
-    hipLaunchKernelGGL((decode_fast_main<D, G, kSmallWaves>), dim3(a.n_waves / kSmallWaves),
-                       dim3(kSmallWaves * 64), 0, s, a);
-  else
-    hipLaunchKernelGGL((decode_fast_main<D, G, kMainWaves>), dim3(a.n_waves / kMainWaves),
-                       dim3(kMainThreads), 0, s, a);
-  hipLaunchKernelGGL((decode_fast_combine<G>), dim3((a.B * a.Hq + 3) / 4), dim3(256), 0, s, a);
+static void launch_fast(const DecodeArgs& a, hipStream_t s, int phase = 3) {
+  if (phase & 1) {
+    if (a.wg_waves == kSmallWaves)
+      hipLaunchKernelGGL((decode_fast_main<D, G, kSmallWaves>), dim3(a.n_waves / kSmallWaves),
+                         dim3(kSmallWaves * 64), 0, s, a);
+    else
+      hipLaunchKernelGGL((decode_fast_main<D, G, kMainWaves>), dim3(a.n_waves / kMainWaves),
+                         dim3(kMainThreads), 0, s, a);
+  }
+  if (phase & 2)
+    hipLaunchKernelGGL((decode_fast_combine<G>), dim3((a.B * a.Hq + 3) / 4), dim3(256), 0, s, a);
 }
 
 template <int D, int G>
@@ -901,25 +905,29 @@ int decode_fast_waves_per_cu(int d, int G) {
   return cached;
 }
 
-hipError_t launch_decode_fast(const DecodeArgs& a, hipStream_t s) {
+static hipError_t launch_fast_phase(const DecodeArgs& a, hipStream_t s, int phase) {
   const int G = a.Hq / a.Hkv;
   if (a.d == 128) {
     switch (G) {
-      case 1: launch_fast<128, 1>(a, s); break;
-      case 2: launch_fast<128, 2>(a, s); break;
-      case 4: launch_fast<128, 4>(a, s); break;
-      default: launch_fast<128, 8>(a, s); break;
+      case 1: launch_fast<128, 1>(a, s, phase); break;
+      case 2: launch_fast<128, 2>(a, s, phase); break;
+      case 4: launch_fast<128, 4>(a, s, phase); break;
+      default: launch_fast<128, 8>(a, s, phase); break;
     }
   } else {
     switch (G) {
-      case 1: launch_fast<64, 1>(a, s); break;
-      case 2: launch_fast<64, 2>(a, s); break;
-      case 4: launch_fast<64, 4>(a, s); break;
-      default: launch_fast<64, 8>(a, s); break;
+      case 1: launch_fast<64, 1>(a, s, phase); break;
+      case 2: launch_fast<64, 2>(a, s, phase); break;
+      case 4: launch_fast<64, 4>(a, s, phase); break;
+      default: launch_fast<64, 8>(a, s, phase); break;
     }
   }
   return hipGetLastError();
 }
+
+hipError_t launch_decode_fast(const DecodeArgs& a, hipStream_t s) { return launch_fast_phase(a, s, 3); }
+hipError_t launch_decode_fast_main(const DecodeArgs& a, hipStream_t s) { return launch_fast_phase(a, s, 1); }
+hipError_t launch_decode_fast_merge(const DecodeArgs& a, hipStream_t s) { return launch_fast_phase(a, s, 2); }
 
 bool hier_fast_path(int dtype, int d) { return dtype == 0 && (d == 64 || d == 128); }
 

@@ -32,8 +32,8 @@ struct DecodeArgs {
   float* out;
   float* out_lse;
   int32_t* out_idx;
-  // MFMA path
-  int n_waves;           // persistent waves (multiple of kMainWaves)
+  // MFMA path (the planner's choice: n_waves > 0)
+  int n_waves;           // persistent waves (multiple of kMainWaves); 0 on the VALU path
   int wg_waves;          // waves per workgroup of the main launch: kMainWaves, or
                          // kSmallWaves when every work unit has a wave of its own
   int uph;               // argmax keys per (head, sequence): ceil(K / 64) units
@@ -58,6 +58,11 @@ constexpr int kSmallWaves = 4;       // waves per workgroup when the grid has a 
 bool decode_fast_path(int dtype, int d, int G, int K, int64_t kv_tok_stride, int max_kv_len);
 int decode_fast_waves_per_cu(int d, int G);  // resident waves per CU of the MFMA main kernel
 hipError_t launch_decode_fast(const DecodeArgs& a, hipStream_t s);
+// the two launches of launch_decode_fast, for callers that split the step:
+// the main grid (scoring, lookup keys, local attention -> partial states),
+// then the merge
+hipError_t launch_decode_fast_main(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_decode_fast_merge(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t s);
 
 // ---- hierarchical lookup ------------------------------------------------------

@@ -64,7 +64,7 @@ enum asm_status_code {
 enum asm_dtype { ASM_BF16 = 0, ASM_F32 = 1 };
 
 /* ABI version of this header (bumped on any signature change). */
-#define ASM_ABI_VERSION 7
+#define ASM_ABI_VERSION 8
 int asm_abi_version(void);
 
 /* Static text for a status code. */
@@ -128,6 +128,41 @@ int asm_decode_step(int dtype, int B, int Hq, int Hkv, int d, int K, float scale
                     const int32_t* kv_start, const int32_t* kv_len, int max_kv_len,
                     float* out, float* out_lse, int32_t* out_idx,
                     void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * asm_decode_step_begin, asm_decode_step_finish -- asm_decode_step as its
+ * two launches, for callers that place other work, or a timer, between
+ * them ([TS] Fase de Inferencia Online: Recuperación and the local
+ * attention in the first, Fusión in the second).
+ *   _begin  the main grid: the centroid scoring (the per-unit argmax keys)
+ *           and the split-K attention over the local tokens (the partial
+ *           states), both into the workspace; out is not touched.
+ *   _finish the merge: the index from the keys, the gather of the memory
+ *           state and the online-softmax merge with the partial states into
+ *           out, out_lse and out_idx.
+ * Both take exactly the arguments of asm_decode_step.  Called on one
+ * stream, _begin then _finish, with the same arguments and workspace (and
+ * nothing writing the workspace or the inputs in between), they compute
+ * what asm_decode_step computes, with the same reproducibility.
+ * Only for steps on the MFMA path in one launch: bf16, d in {64, 128},
+ * Hq/Hkv in {1, 2, 4, 8}, each sequence's KV rows within 2 GiB, at most 2048
+ * sequences; otherwise ASM_ERR_SHAPE before any launch.  The workspace size
+ * is asm_decode_step_ws.
+ */
+int asm_decode_step_begin(int dtype, int B, int Hq, int Hkv, int d, int K, float scale,
+                          const void* q, const void* C, const float* cinv, const float* Abar,
+                          const float* LSEbar, const void* Kl, const void* Vl,
+                          int64_t kv_head_stride, int64_t kv_tok_stride, int64_t kv_capacity,
+                          const int32_t* kv_start, const int32_t* kv_len, int max_kv_len,
+                          float* out, float* out_lse, int32_t* out_idx,
+                          void* ws, size_t ws_bytes, hipStream_t stream);
+int asm_decode_step_finish(int dtype, int B, int Hq, int Hkv, int d, int K, float scale,
+                           const void* q, const void* C, const float* cinv, const float* Abar,
+                           const float* LSEbar, const void* Kl, const void* Vl,
+                           int64_t kv_head_stride, int64_t kv_tok_stride, int64_t kv_capacity,
+                           const int32_t* kv_start, const int32_t* kv_len, int max_kv_len,
+                           float* out, float* out_lse, int32_t* out_idx,
+                           void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * asm_decode_step_noalloc -- asm_decode_step without a workspace, for

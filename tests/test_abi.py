@@ -41,9 +41,9 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_text():
     L = api.lib()
-    assert L.asm_abi_version() == 7
+    assert L.asm_abi_version() == 8
     text = open(HEADER).read()
-    assert int(re.search(r"#define ASM_ABI_VERSION (\d+)", text).group(1)) == 7
+    assert int(re.search(r"#define ASM_ABI_VERSION (\d+)", text).group(1)) == 8
     assert L.asm_status_str(0) == b"ok"
     assert L.asm_status_str(-5).startswith(b"workspace")
 
@@ -83,6 +83,39 @@ def test_decode_validation_errors_before_any_launch():
     need = L.asm_decode_step_ws(0, 1, 4, 2, 128, 16, 64)
     assert need > 0
     assert _decode(ws=1 << 20, wsb=need - 1) == -5
+
+
+def _decode_phase(name, **over):
+    args = dict(dtype=0, B=1, Hq=4, Hkv=2, d=128, K=16, scale=0.1, q=1 << 20, C=1 << 20,
+                cinv=1 << 20, Abar=1 << 20, LSEbar=1 << 20, Kl=1 << 20, Vl=1 << 20, hs=128 * 64,
+                ts=128, cap=64, ks=1 << 20, kn=1 << 20, m=64, out=1 << 20, lse=NULL, idx=NULL,
+                ws=NULL, wsb=0)
+    args.update(over)
+    a = args
+    return getattr(api.lib(), name)(a["dtype"], a["B"], a["Hq"], a["Hkv"], a["d"], a["K"],
+                                     a["scale"], a["q"], a["C"], a["cinv"], a["Abar"],
+                                     a["LSEbar"], a["Kl"], a["Vl"], a["hs"], a["ts"], a["cap"],
+                                     a["ks"], a["kn"], a["m"], a["out"], a["lse"], a["idx"],
+                                     a["ws"], a["wsb"], None)
+
+
+def test_decode_two_launches_validate_like_the_step_and_need_the_mfma_path():
+    """asm_decode_step_begin / _finish check the step's arguments, then refuse
+    what the MFMA path in one launch cannot take (float32, d=96, more than
+    2048 sequences), all before any launch."""
+    L = api.lib()
+    for name in ("asm_decode_step_begin", "asm_decode_step_finish"):
+        assert _decode_phase(name, dtype=5) == -3
+        assert _decode_phase(name, q=NULL) == -1
+        assert _decode_phase(name, ts=12) == -4
+        assert _decode_phase(name) == -5            # a workspace is needed
+        ws = L.asm_decode_step_ws(1, 1, 4, 2, 128, 16, 64)
+        assert _decode_phase(name, dtype=1, ws=1 << 20, wsb=ws) == -2
+        assert b"two launches" in L.asm_last_error()
+        ws = L.asm_decode_step_ws(0, 1, 4, 2, 96, 16, 64)
+        assert _decode_phase(name, d=96, hs=96 * 64, ts=96, ws=1 << 20, wsb=ws) == -2
+        ws = L.asm_decode_step_ws(0, 2049, 4, 2, 128, 16, 64)
+        assert _decode_phase(name, B=2049, ws=1 << 20, wsb=ws) == -2
 
 
 def _decode_noalloc(**over):
