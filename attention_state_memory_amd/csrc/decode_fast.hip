@@ -763,7 +763,12 @@ __global__ void __launch_bounds__(256) decode_fast_combine(DecodeArgs a) {
   if (lane == 0 && a.out_idx) a.out_idx[item] = int32_t(k);
   float* o = a.out + size_t(item) * D;
   const int dd = 2 * lane;
-  if (!valid || k >= uint32_t(a.K)) {
+  // the pieces must lie in the workspace's partial-state rows (they do
+  // whenever the main grid of this step ran on this workspace; a tile
+  // prefix it did not write must not send the loads elsewhere)
+  const int64_t pieces = int64_t(a.n_waves) + 2 * int64_t(a.B) * a.Hkv;
+  const bool placed = nt >= 0 && p0 >= 0 && np >= 0 && p0 + np <= pieces;
+  if (!valid || !placed || k >= uint32_t(a.K)) {
     if (dd < D) *reinterpret_cast<float2*>(o + dd) = make_float2(NAN, NAN);
     if (lane == 0 && a.out_lse) a.out_lse[item] = NAN;
     return;

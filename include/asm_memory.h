@@ -143,7 +143,9 @@ int asm_decode_step(int dtype, int B, int Hq, int Hkv, int d, int K, float scale
  * Both take exactly the arguments of asm_decode_step.  Called on one
  * stream, _begin then _finish, with the same arguments and workspace (and
  * nothing writing the workspace or the inputs in between), they compute
- * what asm_decode_step computes, with the same reproducibility.
+ * what asm_decode_step computes, with the same reproducibility.  _finish on
+ * a workspace that no _begin of this shape filled gives unspecified
+ * outputs, but reads nothing outside the workspace and the inputs.
  * Only for steps on the MFMA path in one launch: bf16, d in {64, 128},
  * Hq/Hkv in {1, 2, 4, 8}, each sequence's KV rows within 2 GiB, at most 2048
  * sequences; otherwise ASM_ERR_SHAPE before any launch.  The workspace size
