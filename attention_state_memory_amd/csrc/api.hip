@@ -81,6 +81,8 @@ struct DecodePlan {
   bool fast = false;
   int Bc = 0;  // sequences per launch
   int n_waves = 0, wg_waves = 0, uph = 0, score_uph = 0;  // MFMA path
+  int direct = 0, mt = 0, gather = 0;                     // MFMA path, small steps
+  size_t off_ca = 0, off_cl = 0;
   int split_tok = 0, S_max = 0, score_tiles = 0;  // VALU path
   size_t off_keys = 0, off_tp = 0, off_pa = 0, off_pl = 0, total = 0;
 };
@@ -133,6 +135,13 @@ DecodePlan plan_decode(int dtype, int B, int Hq, int Hkv, int d, int K, int max_
     // a wave for every unit (whatever the actual lengths, the roles are then
     // disjoint): smaller workgroups spread the grid over more compute units
     p.wg_waves = w >= units ? asmk::kSmallWaves : asmk::kMainWaves;
+    // With a wave for every potential unit, tile t of segment s is wave and
+    // slot s * mt + t (direct layout: no scan of the lengths); with at most
+    // 16 units per head and 8 sequences, the scoring units also gather their
+    // best entries' states, so the merge needs one round of loads.
+    p.direct = p.wg_waves == asmk::kSmallWaves ? 1 : 0;
+    p.mt = int((int64_t(max_kv_len) + 31) / 32);
+    p.gather = p.direct && score_uph > 0 && score_uph <= 16 && p.Bc <= 8 ? 1 : 0;
     p.off_keys = off;
     off = asmk::align_up(off + size_t(Hq) * p.Bc * p.uph * sizeof(uint64_t), kAlign);
     p.off_tp = off;
@@ -143,6 +152,12 @@ DecodePlan plan_decode(int dtype, int B, int Hq, int Hkv, int d, int K, int max_
     off = asmk::align_up(off + pieces * G * d * sizeof(float), kAlign);
     p.off_pl = off;
     off = asmk::align_up(off + pieces * G * sizeof(float), kAlign);
+    if (p.gather) {
+      p.off_ca = off;
+      off = asmk::align_up(off + size_t(Hq) * p.Bc * p.uph * d * sizeof(float), kAlign);
+      p.off_cl = off;
+      off = asmk::align_up(off + size_t(Hq) * p.Bc * p.uph * sizeof(float), kAlign);
+    }
   } else {
     p.Bc = B;
     p.split_tok = decode_split_tokens(B, Hkv, max_kv_len);
@@ -241,12 +256,15 @@ int decode_impl(int dtype, int B, int Hq, int Hkv, int d, int K, float scale,
   a.max_kv_len = max_kv_len;
   a.no_memory = attend_only ? 1 : 0;
   a.n_waves = p.n_waves; a.wg_waves = p.wg_waves; a.uph = p.uph; a.score_uph = p.score_uph;
+  a.direct = p.direct; a.mt = p.mt; a.gather = p.gather;
   a.split_tok = p.split_tok; a.S_max = p.S_max; a.score_tiles = p.score_tiles;
   char* w = static_cast<char*>(ws);
   a.keys = reinterpret_cast<uint64_t*>(w + p.off_keys);
   a.tile_prefix = reinterpret_cast<int32_t*>(w + p.off_tp);
   a.part_a = reinterpret_cast<float*>(w + p.off_pa);
   a.part_lse = reinterpret_cast<float*>(w + p.off_pl);
+  a.cand_a = p.gather ? reinterpret_cast<float*>(w + p.off_ca) : nullptr;
+  a.cand_l = p.gather ? reinterpret_cast<float*>(w + p.off_cl) : nullptr;
   const size_t esz = dtype == ASM_BF16 ? 2 : 4;
   int32_t* probes_base = hier ? hier->probes_out : nullptr;
   // Sequences are independent: batches larger than one launch's limit run

@@ -240,6 +240,57 @@ __device__ __forceinline__ void score_unit(const DecodeArgs& a, int64_t u, int S
   }
 }
 
+// One unit in the direct layout's gathering steps (at most 8 sequences): its
+// keys, and for every sequence the state (a row, lse) of the unit's best
+// entry, copied to the unit's candidate slot, so that the merge finds the
+// winner's state in the same round as the keys.  (Every unit holds a row
+// below K, so its best key names an entry; an entry index past K is skipped
+// all the same.)
+template <int D>
+__device__ __forceinline__ void score_unit_gather(const DecodeArgs& a, int64_t u, int SV) {
+  const int lane = threadIdx.x & 63;
+  const int r16 = lane & 15, grp = lane >> 4;
+  const int h = int(u / a.uph), j = int(u - int64_t(h) * a.uph);
+  u32x4 qb[2][D / 32];
+  load_queries<D>(qb, a, h, 0);
+  uint64_t best[2] = {0ull, 0ull};
+  ScoreHalf<D> t0, t1;
+  load_half<D>(t0, a, int(2 * u), SV);
+  load_half<D>(t1, a, int(2 * u + 1), SV);
+  consume_half<D>(t0, qb, a, 64 * j, best);
+  consume_half<D>(t1, qb, a, 64 * j + 32, best);
+  // lane (r16, *) now reduces sequence r16's key (at most 8 sequences: the
+  // first column tile only)
+  uint64_t kq = best[0];
+  kq = umax64(kq, shfl_xor_u64(kq, 16));
+  kq = umax64(kq, shfl_xor_u64(kq, 32));
+  if (grp == 0 && r16 < a.B) a.keys[(size_t(h) * a.B + r16) * a.uph + j] = kq;
+  // the best entries' states: all loads first (sequences past B repeat the
+  // last one), then the stores
+  const int dd = 2 * lane;
+  float2 va[8];
+  float vl[8];
+  uint32_t ev[8];
+#pragma unroll
+  for (int b = 0; b < 8; ++b) {
+    const int bb = b < a.B ? b : a.B - 1;
+    const uint32_t e = key_index((uint64_t(uint32_t(__builtin_amdgcn_readlane(int(kq >> 32), bb))) << 32) |
+                                 uint32_t(__builtin_amdgcn_readlane(int(uint32_t(kq)), bb)));
+    ev[b] = e;
+    const size_t row = size_t(h) * a.K + (e < uint32_t(a.K) ? e : 0u);
+    va[b] = dd < D ? *reinterpret_cast<const float2*>(a.Abar + row * D + dd) : make_float2(0.f, 0.f);
+    vl[b] = a.LSEbar[row];
+  }
+#pragma unroll
+  for (int b = 0; b < 8; ++b) {
+    if (b < a.B && ev[b] < uint32_t(a.K)) {
+      const size_t c = (size_t(h) * a.B + b) * a.uph + j;
+      if (dd < D) *reinterpret_cast<float2*>(a.cand_a + c * D + dd) = va[b];
+      if (lane == 0) a.cand_l[c] = vl[b];
+    }
+  }
+}
+
 // The run of scoring units this wave claims, starting with the claimed item
 // v (a unit); returns the first claimed item that ends the run (a tile, a
 // unit of another head, or -1).  With at most 32 sequences the queries of
@@ -604,6 +655,43 @@ __device__ __forceinline__ void run_pool(const DecodeArgs& a, const SeqTab& S, P
   }
 }
 
+// The work of wave gw in the direct layout (a wave for every potential work
+// unit): scoring unit gw - (W - SU) for the last SU waves; otherwise tile t
+// of segment s for gw = s * mt + t, whose partial state goes to slot gw (an
+// empty one past the sequence's end).  The wave reads its sequence's length
+// and first slot itself, so no wave scans the lengths.  `ctr` is the wave's
+// counter in LDS, set so that the tile's run claims nothing more.
+template <int D, int G>
+__device__ __forceinline__ void direct_wave(const DecodeArgs& a, int64_t gw, int32_t* ctr,
+                                            char* vlds) {
+  const int lane = threadIdx.x & 63;
+  const int64_t W = a.n_waves;
+  const int64_t SU = int64_t(a.Hq) * a.score_uph;
+  const int64_t su = gw - (W - SU);
+  if (su >= 0) {
+    if (a.gather)
+      score_unit_gather<D>(a, su, int(2 * SU));
+    else
+      score_unit<D>(a, su, int(2 * SU));
+    return;
+  }
+  if (gw >= int64_t(a.B) * a.Hkv * a.mt) return;
+  const int seg = int(gw / a.mt);
+  const int t = int(gw - int64_t(seg) * a.mt);
+  const int b = seg / a.Hkv, g = seg - b * a.Hkv;
+  const int n = a.kv_len[b], st = a.kv_start[b];
+  const bool valid = n >= 0 && n <= a.max_kv_len && st >= 0 && int64_t(st) + n <= a.kv_capacity;
+  const int nt = valid ? (n + 31) >> 5 : 0;
+  if (t >= nt) {
+    if (lane < G) a.part_lse[size_t(gw) * G + lane] = -INFINITY;
+    return;
+  }
+  if (lane == 0) *ctr = 1;  // the run's next claim finds the one-item pool taken
+  PairPool pool{ctr, 1, 0, 0, gw, 0, 1};
+  const SegLoc L{b, g, nt, int64_t(seg) * a.mt, n, st};
+  attn_run<D, G>(a, L, gw, pool, gw, vlds);
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -623,6 +711,10 @@ __device__ __forceinline__ void main_block(const DecodeArgs& a, int blk) {
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
   const int64_t gw = int64_t(blk) * NW + w;
+  if (a.direct) {  // the same for the whole grid: no wave reaches a barrier
+    direct_wave<D, G>(a, gw, &ctr[w], vls + w * Tile<D, G>::kVBytes);
+    return;
+  }
   const int64_t W = a.n_waves;
   const int64_t SU = int64_t(a.Hq) * a.score_uph;
   if (threadIdx.x < NW) ctr[threadIdx.x] = 0;
@@ -723,6 +815,79 @@ decode_fast_main_hier(DecodeArgs a, HierArgs h, int lookup_blocks) {
     main_block<D, G, NW>(a, int(blockIdx.x) - lookup_blocks);
 }
 
+// The first 64 piece rows of a segment, in groups of 16 rows as far as the
+// segment has pieces (rows past the last piece read as zeros through the
+// buffer bounds).
+template <int G>
+__device__ __forceinline__ void load_piece_rows(u32x2 (&r0)[64], __amdgpu_buffer_rsrc_t rp,
+                                                int64_t np, int D, int dd) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (np > 16 * j) {
+#pragma unroll
+      for (int i = 16 * j; i < 16 * j + 16; ++i)
+        r0[i] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                                              rp, int((i * G * D + dd) * 4), 0, 0));
+    }
+  }
+}
+
+// The online-softmax merge of item (b, h): the memory state (lm, am) with
+// the np pieces of its segment (slots p0 .. p0 + np - 1, the first 64 rows
+// already loaded in r0, their normalisers lc0 on lanes 0..63), written to
+// out and out_lse.
+template <int G>
+__device__ __forceinline__ void merge_item(const DecodeArgs& a, int item, int hh, int D, int dd,
+                                           float lm, float2 am, float lc0, const u32x2 (&r0)[64],
+                                           int64_t p0, int64_t np, __amdgpu_buffer_rsrc_t rp) {
+  const int lane = threadIdx.x & 63;
+  float* o = a.out + size_t(item) * D;
+  float M = fmaxf(lm, lc0);
+  for (int64_t c = 64 + lane; c < np; c += 64) M = fmaxf(M, a.part_lse[(p0 + c) * G + hh]);
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, shfl_xor_f(M, m));
+  if (M == -INFINITY) {
+    if (dd < D) *reinterpret_cast<float2*>(o + dd) = make_float2(0.f, 0.f);
+    if (lane == 0 && a.out_lse) a.out_lse[item] = -INFINITY;
+    return;
+  }
+  const float wm = lm == -INFINITY ? 0.0f : expf(lm - M);
+  float v0 = wm > 0.0f ? wm * am.x : 0.0f, v1 = wm > 0.0f ? wm * am.y : 0.0f;
+  // an empty piece (weight 0) may hold stale values: skip it
+  const auto acc = [&](float wi, const u32x2& r) {
+    v0 = wi > 0.0f ? fmaf(wi, __uint_as_float(r[0]), v0) : v0;
+    v1 = wi > 0.0f ? fmaf(wi, __uint_as_float(r[1]), v1) : v1;
+  };
+  const float wc0 = lc0 == -INFINITY ? 0.0f : expf(lc0 - M);
+  float zsum = wc0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (np > 16 * j) {
+#pragma unroll
+      for (int i = 16 * j; i < 16 * j + 16; ++i) acc(readlane_f(wc0, i), r0[i]);
+    }
+  }
+  for (int64_t c64 = 64; c64 < np; c64 += 64) {
+    const float lc = c64 + lane < np ? a.part_lse[(p0 + c64 + lane) * G + hh] : -INFINITY;
+    const float wc = lc == -INFINITY ? 0.0f : expf(lc - M);
+    zsum += wc;
+    const int64_t cend = min<int64_t>(np, c64 + 64);
+    for (int64_t c = c64; c < cend; c += 16) {
+      u32x2 r[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        r[i] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                                             rp, int(((c + i) * G * D + dd) * 4), 0, 0));
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc(readlane_f(wc, int(c - c64) + i), r[i]);
+    }
+  }
+  const float Z = wm + wave_sum(zsum);
+  const float inv = 1.0f / Z;
+  if (dd < D) *reinterpret_cast<float2*>(o + dd) = make_float2(v0 * inv, v1 * inv);
+  if (lane == 0 && a.out_lse) a.out_lse[item] = M + logf(Z);
+}
+
 // One wave per (b, h): index from the unit keys, gather of the memory
 // state, merge with the partial states of segment (b, h / G).  The loads are
 // arranged in two dependent rounds: (1) sequence bounds, tile prefix, keys;
@@ -780,65 +945,77 @@ __global__ void __launch_bounds__(256) decode_fast_combine(DecodeArgs a) {
                         : make_float2(0.f, 0.f);
   const float* pa0 = a.part_a + (p0 * G + hh) * D;
   const auto rp = make_rsrc(pa0, np > 0 ? uint32_t(((np - 1) * G + 1) * D * 4) : 0u);
-  // the first 64 piece normalisers and piece rows load with the memory state,
-  // in groups of 16 rows as far as the segment has pieces (rows past the
-  // last piece read as zeros); a segment split over many waves (a long
-  // context at small batch) thus merges its first 64 pieces after one round
+  // the first 64 piece normalisers and piece rows load with the memory state;
+  // a segment split over many waves (a long context at small batch) thus
+  // merges its first 64 pieces after one round
   const float lc0 = lane < np ? a.part_lse[(p0 + lane) * G + hh] : -INFINITY;
   u32x2 r0[64];
+  load_piece_rows<G>(r0, rp, np, D, dd);
+  merge_item<G>(a, item, hh, D, dd, lm, am, lc0, r0, p0, np, rp);
+}
+
+// The merge in the direct layout: segment (b, g)'s pieces are slots
+// (b*Hkv + g)*mt .. +mt (those past the sequence's end empty), known without
+// the tile prefix, so they load in the first round with the keys; with
+// gathering, so do the units' candidate states, and the winner's state is the
+// candidate of the unit that holds the winning entry.  One dependent round of
+// loads in all (two without gathering: the memory state).
+template <int G>
+__global__ void __launch_bounds__(256) decode_fast_combine_direct(DecodeArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int item = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (item >= a.B * a.Hq) return;
+  const int b = item / a.Hq, h = item % a.Hq;
+  const int g = h / G, hh = h % G;
+  const int D = a.d;
+  const int dd = 2 * lane;
+  const bool valid = seq_valid(a, b);
+  const uint64_t* kk = a.keys + (size_t(h) * a.B + b) * a.uph;
+  uint64_t best = 0;
+  if (!a.no_memory)
+    for (int u = lane; u < a.uph; u += 64) best = umax64(best, kk[u]);
+  const int64_t p0 = (int64_t(b) * a.Hkv + g) * a.mt, np = a.mt;
+  const float* pa0 = a.part_a + (p0 * G + hh) * D;
+  const auto rp = make_rsrc(pa0, np > 0 ? uint32_t(((np - 1) * G + 1) * D * 4) : 0u);
+  const float lc0 = lane < np ? a.part_lse[(p0 + lane) * G + hh] : -INFINITY;
+  u32x2 r0[64];
+  load_piece_rows<G>(r0, rp, np, D, dd);
+  // candidates: unit j's best entry state for this (h, b), j < uph <= 16
+  u32x2 cr[16];
+  float cl = -INFINITY;
+  if (a.gather) {
+    const size_t c0 = (size_t(h) * a.B + b) * a.uph;
+    const auto rc = make_rsrc(a.cand_a + c0 * D, uint32_t(a.uph) * D * 4);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    if (np > 16 * j) {
-#pragma unroll
-      for (int i = 16 * j; i < 16 * j + 16; ++i)
-        r0[i] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
-                                              rp, int((i * G * D + dd) * 4), 0, 0));
-    }
+    for (int j = 0; j < 16; ++j)
+      cr[j] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rc, int((j * D + dd) * 4), 0, 0));
+    cl = lane < a.uph ? a.cand_l[c0 + lane] : -INFINITY;
   }
-  float M = fmaxf(lm, lc0);
-  for (int64_t c = 64 + lane; c < np; c += 64) M = fmaxf(M, a.part_lse[(p0 + c) * G + hh]);
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, shfl_xor_f(M, m));
-  if (M == -INFINITY) {
-    if (dd < D) *reinterpret_cast<float2*>(o + dd) = make_float2(0.f, 0.f);
-    if (lane == 0 && a.out_lse) a.out_lse[item] = -INFINITY;
+  best = wave_max_u64(best);
+  const uint32_t k = a.no_memory ? 0u : __builtin_amdgcn_readfirstlane(key_index(best));
+  if (lane == 0 && a.out_idx) a.out_idx[item] = int32_t(k);
+  if (!valid || k >= uint32_t(a.K)) {
+    float* o = a.out + size_t(item) * D;
+    if (dd < D) *reinterpret_cast<float2*>(o + dd) = make_float2(NAN, NAN);
+    if (lane == 0 && a.out_lse) a.out_lse[item] = NAN;
     return;
   }
-  const float wm = lm == -INFINITY ? 0.0f : expf(lm - M);
-  float v0 = wm > 0.0f ? wm * am.x : 0.0f, v1 = wm > 0.0f ? wm * am.y : 0.0f;
-  // an empty piece (weight 0) may hold stale values: skip it
-  const auto acc = [&](float wi, const u32x2& r) {
-    v0 = wi > 0.0f ? fmaf(wi, __uint_as_float(r[0]), v0) : v0;
-    v1 = wi > 0.0f ? fmaf(wi, __uint_as_float(r[1]), v1) : v1;
-  };
-  const float wc0 = lc0 == -INFINITY ? 0.0f : expf(lc0 - M);
-  float zsum = wc0;
+  float lm = -INFINITY;
+  float2 am = make_float2(0.f, 0.f);
+  if (!a.no_memory) {
+    if (a.gather) {
+      const int js = int(k >> 6);  // the unit holding entry k
+      u32x2 sel = cr[0];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    if (np > 16 * j) {
-#pragma unroll
-      for (int i = 16 * j; i < 16 * j + 16; ++i) acc(readlane_f(wc0, i), r0[i]);
+      for (int j = 1; j < 16; ++j) sel = j == js ? cr[j] : sel;
+      lm = readlane_f(cl, js);
+      if (dd < D) am = make_float2(__uint_as_float(sel[0]), __uint_as_float(sel[1]));
+    } else {
+      lm = a.LSEbar[size_t(h) * a.K + k];
+      if (dd < D) am = *reinterpret_cast<const float2*>(a.Abar + (size_t(h) * a.K + k) * D + dd);
     }
   }
-  for (int64_t c64 = 64; c64 < np; c64 += 64) {
-    const float lc = c64 + lane < np ? a.part_lse[(p0 + c64 + lane) * G + hh] : -INFINITY;
-    const float wc = lc == -INFINITY ? 0.0f : expf(lc - M);
-    zsum += wc;
-    const int64_t cend = min<int64_t>(np, c64 + 64);
-    for (int64_t c = c64; c < cend; c += 16) {
-      u32x2 r[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-        r[i] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
-                                             rp, int(((c + i) * G * D + dd) * 4), 0, 0));
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc(readlane_f(wc, int(c - c64) + i), r[i]);
-    }
-  }
-  const float Z = wm + wave_sum(zsum);
-  const float inv = 1.0f / Z;
-  if (dd < D) *reinterpret_cast<float2*>(o + dd) = make_float2(v0 * inv, v1 * inv);
-  if (lane == 0 && a.out_lse) a.out_lse[item] = M + logf(Z);
+  merge_item<G>(a, item, hh, D, dd, lm, am, lc0, r0, p0, np, rp);
 }
 
 // ---------------------------------------------------------------------------
@@ -861,7 +1038,10 @@ static void launch_fast_hier(const DecodeArgs& a, const HierArgs& h, hipStream_t
     hipLaunchKernelGGL((decode_fast_main_hier<D, G, kMainWaves>),
                        dim3(unsigned(lookup_blocks + a.n_waves / kMainWaves)), dim3(kMainThreads), 0,
                        s, a, h, lookup_blocks);
-  hipLaunchKernelGGL((decode_fast_combine<G>), dim3((a.B * a.Hq + 3) / 4), dim3(256), 0, s, a);
+  if (a.direct)
+    hipLaunchKernelGGL((decode_fast_combine_direct<G>), dim3((a.B * a.Hq + 3) / 4), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((decode_fast_combine<G>), dim3((a.B * a.Hq + 3) / 4), dim3(256), 0, s, a);
 }
 
 // phase bit 1: the main grid; bit 2: the merge
@@ -875,8 +1055,12 @@ static void launch_fast(const DecodeArgs& a, hipStream_t s, int phase = 3) {
       hipLaunchKernelGGL((decode_fast_main<D, G, kMainWaves>), dim3(a.n_waves / kMainWaves),
                          dim3(kMainThreads), 0, s, a);
   }
-  if (phase & 2)
-    hipLaunchKernelGGL((decode_fast_combine<G>), dim3((a.B * a.Hq + 3) / 4), dim3(256), 0, s, a);
+  if (phase & 2) {
+    if (a.direct)
+      hipLaunchKernelGGL((decode_fast_combine_direct<G>), dim3((a.B * a.Hq + 3) / 4), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((decode_fast_combine<G>), dim3((a.B * a.Hq + 3) / 4), dim3(256), 0, s, a);
+  }
 }
 
 template <int D, int G>
