@@ -77,11 +77,13 @@ int check_ws(const void* ws, size_t ws_bytes, size_t need) {
   } while (0)
 
 // ---- decode planning -------------------------------------------------------
+// Direct layout (small steps): local tiles per wave and per partial state.
+constexpr int kDirectTilesPerWave = 2;
 struct DecodePlan {
   bool fast = false;
   int Bc = 0;  // sequences per launch
   int n_waves = 0, wg_waves = 0, uph = 0, score_uph = 0;  // MFMA path
-  int direct = 0, mt = 0, gather = 0;                     // MFMA path, small steps
+  int direct = 0, mt = 0, tpw = 1, mp = 0, gather = 0;    // MFMA path, small steps
   size_t off_ca = 0, off_cl = 0;
   int split_tok = 0, S_max = 0, score_tiles = 0;  // VALU path
   size_t off_keys = 0, off_tp = 0, off_pa = 0, off_pl = 0, total = 0;
@@ -141,6 +143,8 @@ DecodePlan plan_decode(int dtype, int B, int Hq, int Hkv, int d, int K, int max_
     // best entries' states, so the merge needs one round of loads.
     p.direct = p.wg_waves == asmk::kSmallWaves ? 1 : 0;
     p.mt = int((int64_t(max_kv_len) + 31) / 32);
+    p.tpw = kDirectTilesPerWave;
+    p.mp = (p.mt + p.tpw - 1) / p.tpw;
     p.gather = p.direct && score_uph > 0 && score_uph <= 16 && p.Bc <= 8 ? 1 : 0;
     p.off_keys = off;
     off = asmk::align_up(off + size_t(Hq) * p.Bc * p.uph * sizeof(uint64_t), kAlign);
@@ -256,7 +260,7 @@ int decode_impl(int dtype, int B, int Hq, int Hkv, int d, int K, float scale,
   a.max_kv_len = max_kv_len;
   a.no_memory = attend_only ? 1 : 0;
   a.n_waves = p.n_waves; a.wg_waves = p.wg_waves; a.uph = p.uph; a.score_uph = p.score_uph;
-  a.direct = p.direct; a.mt = p.mt; a.gather = p.gather;
+  a.direct = p.direct; a.mt = p.mt; a.tpw = p.tpw; a.mp = p.mp; a.gather = p.gather;
   a.split_tok = p.split_tok; a.S_max = p.S_max; a.score_tiles = p.score_tiles;
   char* w = static_cast<char*>(ws);
   a.keys = reinterpret_cast<uint64_t*>(w + p.off_keys);

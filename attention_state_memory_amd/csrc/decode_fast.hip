@@ -656,11 +656,11 @@ __device__ __forceinline__ void run_pool(const DecodeArgs& a, const SeqTab& S, P
 }
 
 // The work of wave gw in the direct layout (a wave for every potential work
-// unit): scoring unit gw - (W - SU) for the last SU waves; otherwise tile t
-// of segment s for gw = s * mt + t, whose partial state goes to slot gw (an
-// empty one past the sequence's end).  The wave reads its sequence's length
-// and first slot itself, so no wave scans the lengths.  `ctr` is the wave's
-// counter in LDS, set so that the tile's run claims nothing more.
+// unit): scoring unit gw - (W - SU) for the last SU waves; otherwise tiles
+// tpw*p .. tpw*p + tpw - 1 of segment s for gw = s * mp + p, whose partial
+// state goes to slot gw (an empty one past the sequence's end).  The wave
+// reads its sequence's length and first slot itself, so no wave scans the
+// lengths.  `ctr` is the wave's counter in LDS.
 template <int D, int G>
 __device__ __forceinline__ void direct_wave(const DecodeArgs& a, int64_t gw, int32_t* ctr,
                                             char* vlds) {
@@ -675,9 +675,9 @@ __device__ __forceinline__ void direct_wave(const DecodeArgs& a, int64_t gw, int
       score_unit<D>(a, su, int(2 * SU));
     return;
   }
-  if (gw >= int64_t(a.B) * a.Hkv * a.mt) return;
-  const int seg = int(gw / a.mt);
-  const int t = int(gw - int64_t(seg) * a.mt);
+  if (gw >= int64_t(a.B) * a.Hkv * a.mp) return;
+  const int seg = int(gw / a.mp);
+  const int t = int(gw - int64_t(seg) * a.mp) * a.tpw;  // first tile of this wave
   const int b = seg / a.Hkv, g = seg - b * a.Hkv;
   const int n = a.kv_len[b], st = a.kv_start[b];
   const bool valid = n >= 0 && n <= a.max_kv_len && st >= 0 && int64_t(st) + n <= a.kv_capacity;
@@ -686,10 +686,13 @@ __device__ __forceinline__ void direct_wave(const DecodeArgs& a, int64_t gw, int
     if (lane < G) a.part_lse[size_t(gw) * G + lane] = -INFINITY;
     return;
   }
-  if (lane == 0) *ctr = 1;  // the run's next claim finds the one-item pool taken
-  PairPool pool{ctr, 1, 0, 0, gw, 0, 1};
+  // a pool of this wave's tiles (tile x = seg*mt + t ..), its first already
+  // taken; the run claims the others (past the sequence's end it stops)
+  const int64_t x = int64_t(seg) * a.mt + t;
+  if (lane == 0) *ctr = 1;
+  PairPool pool{ctr, a.tpw, 0, 0, x, 0, 1};
   const SegLoc L{b, g, nt, int64_t(seg) * a.mt, n, st};
-  attn_run<D, G>(a, L, gw, pool, gw, vlds);
+  attn_run<D, G>(a, L, x, pool, gw, vlds);
 }
 
 }  // namespace
@@ -955,7 +958,7 @@ __global__ void __launch_bounds__(256) decode_fast_combine(DecodeArgs a) {
 }
 
 // The merge in the direct layout: segment (b, g)'s pieces are slots
-// (b*Hkv + g)*mt .. +mt (those past the sequence's end empty), known without
+// (b*Hkv + g)*mp .. +mp (those past the sequence's end empty), known without
 // the tile prefix, so they load in the first round with the keys; with
 // gathering, so do the units' candidate states, and the winner's state is the
 // candidate of the unit that holds the winning entry.  One dependent round of
@@ -974,7 +977,7 @@ __global__ void __launch_bounds__(256) decode_fast_combine_direct(DecodeArgs a) 
   uint64_t best = 0;
   if (!a.no_memory)
     for (int u = lane; u < a.uph; u += 64) best = umax64(best, kk[u]);
-  const int64_t p0 = (int64_t(b) * a.Hkv + g) * a.mt, np = a.mt;
+  const int64_t p0 = (int64_t(b) * a.Hkv + g) * a.mp, np = a.mp;
   const float* pa0 = a.part_a + (p0 * G + hh) * D;
   const auto rp = make_rsrc(pa0, np > 0 ? uint32_t(((np - 1) * G + 1) * D * 4) : 0u);
   const float lc0 = lane < np ? a.part_lse[(p0 + lane) * G + hh] : -INFINITY;

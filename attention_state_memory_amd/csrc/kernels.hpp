@@ -41,11 +41,14 @@ struct DecodeArgs {
                          // the keys were written beforehand (hierarchical lookup)
   int32_t* tile_prefix;  // [B + 1] 32-token tiles per kv head, prefix over sequences
   int no_memory;         // attention only: no lookup, the merge starts from the empty state
-  // direct layout (grids with a wave for every potential work unit): tile t
-  // of segment s (sequence b, kv head g; s = b*Hkv + g) is wave and partial
-  // slot s*mt + t, so neither kernel needs the lengths' prefix
+  // direct layout (grids with a wave for every potential work unit): tiles
+  // tpw*p .. tpw*p + tpw - 1 of segment s (sequence b, kv head g;
+  // s = b*Hkv + g) are wave and partial slot s*mp + p, so neither kernel
+  // needs the lengths' prefix
   int direct;
   int mt;                // ceil(max_kv_len / 32): potential tiles per segment
+  int tpw;               // direct: tiles per wave (and per partial slot)
+  int mp;                // direct: pieces per segment, ceil(mt / tpw)
   int gather;            // direct, at most 16 units per head and 8 sequences: each
                          // scoring unit also gathers its best entry's state
   float* cand_a;         // gather: [Hq, B, uph, d] state of each unit's best entry
