@@ -36,6 +36,28 @@ def test_decode_small_shapes(case):
     check_decode(inp, out, lse, idx)
 
 
+# Steps small enough that every potential work unit has a wave (the direct
+# layout: each wave reads its sequence's bounds itself; two tiles per wave
+# and per partial state; with at most 16 scoring units per head and 8
+# sequences the scoring units also copy their best entries' states).
+DIRECT = [
+    # (seed, d, Hq, Hkv, K, lens)                        what it exercises
+    (20, 128, 32, 8, 1024, [61]),                         # odd tile count: a wave with one tile
+    (21, 128, 32, 8, 1000, [5, 0, 500, 33, 64, 65, 1, 499]),  # 8 sequences (gathering), last unit partial
+    (22, 128, 32, 8, 960, [100] * 9),                     # 9 sequences: no gathering
+    (23, 64, 16, 2, 1024, [31, 32, 33]),                  # d=64, G=8, 16 units per head
+    (24, 128, 8, 8, 1088, [300, 7]),                      # 17 units per head: no gathering, G=1
+    (25, 128, 32, 8, 512, [0, 1]),                        # one empty sequence, one with a single token
+]
+
+
+@pytest.mark.parametrize("case", DIRECT, ids=[f"d{c[0]}" for c in DIRECT])
+def test_decode_direct_layout_shapes(case):
+    inp = _case(*case)
+    out, lse, idx = run_decode_gpu(inp)
+    check_decode(inp, out, lse, idx)
+
+
 def test_decode_float32_tiny_shape():
     """One head, d=64, float32, four queries sharing one 32-token local KV."""
     inp = _case(8, 64, 1, 1, 64, [32], dtype="f32")
