@@ -714,7 +714,10 @@ __device__ __forceinline__ void main_block(const DecodeArgs& a, int blk) {
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
   const int64_t gw = int64_t(blk) * NW + w;
-  if (a.direct) {  // the same for the whole grid: no wave reaches a barrier
+  // The planner takes 4-wave workgroups exactly for the direct layout
+  // (a.direct), so the workgroup size selects it at compile time and the
+  // 8-wave kernel holds none of its code.
+  if constexpr (NW == kSmallWaves) {
     direct_wave<D, G>(a, gw, &ctr[w], vls + w * Tile<D, G>::kVBytes);
     return;
   }

@@ -41,6 +41,15 @@ struct DecodeArgs {
                          // the keys were written beforehand (hierarchical lookup)
   int32_t* tile_prefix;  // [B + 1] 32-token tiles per kv head, prefix over sequences
   int no_memory;         // attention only: no lookup, the merge starts from the empty state
+  // VALU path
+  int split_tok;    // local tokens per attention item
+  int S_max;        // splits per sequence = ceil(max_kv_len / split_tok)
+  int score_tiles;  // ceil(K / 256)
+  // both
+  uint64_t* keys;   // MFMA: [Hq, B, uph]; VALU: [Hq, score_tiles, B]
+  float* part_a;    // MFMA: [n_waves + 2*B*Hkv, G, d]; VALU: [B, Hq, S_max, d]
+  float* part_lse;  // MFMA: [n_waves + 2*B*Hkv, G];    VALU: [B, Hq, S_max]
+  // (last, so that the fields above keep their kernel-argument offsets)
   // direct layout (grids with a wave for every potential work unit): tiles
   // tpw*p .. tpw*p + tpw - 1 of segment s (sequence b, kv head g;
   // s = b*Hkv + g) are wave and partial slot s*mp + p, so neither kernel
@@ -53,14 +62,6 @@ struct DecodeArgs {
                          // scoring unit also gathers its best entry's state
   float* cand_a;         // gather: [Hq, B, uph, d] state of each unit's best entry
   float* cand_l;         // gather: [Hq, B, uph] its lse
-  // VALU path
-  int split_tok;    // local tokens per attention item
-  int S_max;        // splits per sequence = ceil(max_kv_len / split_tok)
-  int score_tiles;  // ceil(K / 256)
-  // both
-  uint64_t* keys;   // MFMA: [Hq, B, uph]; VALU: [Hq, score_tiles, B]
-  float* part_a;    // MFMA: [n_waves + 2*B*Hkv, G, d]; VALU: [B, Hq, S_max, d]
-  float* part_lse;  // MFMA: [n_waves + 2*B*Hkv, G];    VALU: [B, Hq, S_max]
 };
 
 constexpr int kFastMaxBatch = 2048;  // sequences per MFMA-path launch
