@@ -145,6 +145,13 @@ DecodePlan plan_decode(int dtype, int B, int Hq, int Hkv, int d, int K, int max_
     p.mt = int((int64_t(max_kv_len) + 31) / 32);
     p.tpw = kDirectTilesPerWave;
     p.mp = (p.mt + p.tpw - 1) / p.tpw;
+    if (p.direct) {
+      // the direct layout's waves: the scoring units and ceil(mt / tpw) per
+      // segment (fewer workgroups to dispatch than one wave per tile)
+      int64_t wd = int64_t(Hq) * score_uph + int64_t(Bc) * Hkv * p.mp;
+      if (wd < 2) wd = 2;
+      p.n_waves = int((wd + asmk::kMainWaves - 1) / asmk::kMainWaves * asmk::kMainWaves);
+    }
     p.gather = p.direct && score_uph > 0 && score_uph <= 16 && p.Bc <= 8 ? 1 : 0;
     p.off_keys = off;
     off = asmk::align_up(off + size_t(Hq) * p.Bc * p.uph * sizeof(uint64_t), kAlign);
