@@ -178,3 +178,22 @@ def test_decode_hier_batch_beyond_resident_grid():
     ref, ref_lse = O.decode_with_idx(widen(inp["q"]), idx, widen(inp["Abar"]), widen(inp["LSEbar"]),
                                      ks, vs, inp["scale"])
     assert_states_close(out, lse, ref, ref_lse)
+
+
+def test_decode_hier_more_probes_than_supers():
+    """p = 12 probes over S = 8 supers at 5 sequences: the merge reads one
+    candidate state per probe beside the keys, and probe ranks past the
+    non-empty supers find nothing and leave their candidate unwritten.  Every
+    super is probed, so this is the flat search, and the outputs follow the
+    oracle."""
+    inp = _hier_case(6, B=5, Hq=8, Hkv=2, K=512, S=8, lens=[64, 0, 1, 200, 31])
+    index, out, lse, idx, probes = _run_hier(inp, S=8, p=12, iters=2)
+    assert np.all(probes[..., 8:] == -1)
+    q64, C64 = widen(inp["q"]), widen(inp["C"])
+    for h in range(8):
+        _, cs, _ = O.assign(q64[:, h], C64[h])
+        assert np.all(O.accept_index(idx[:, h], cs, GAP_TOL))
+    ks, vs = local_lists(inp)
+    ref, ref_lse = O.decode_with_idx(q64, idx, widen(inp["Abar"]), widen(inp["LSEbar"]), ks, vs,
+                                     inp["scale"])
+    assert_states_close(out, lse, ref, ref_lse)
