@@ -521,6 +521,25 @@ struct SeqTab {
 };
 __device__ __forceinline__ SegLoc locate(const DecodeArgs& a, const SeqTab& S, int64_t x) {
   const int32_t* tp = S.tp;
+  if (a.B < 64) {
+    // One round of LDS reads: lane l holds sequence l's tile prefix, length
+    // and first slot, and the sequence of tile x is the last one whose first
+    // tile is at most x (the tile prefix does not decrease, so those lanes
+    // form a prefix of the wave).  A binary search would take log2(B)
+    // dependent LDS round trips, and this runs at every wave's first tile,
+    // at each segment change and at the end of every pool.
+    const int lane = threadIdx.x & 63;
+    const int32_t tpl = tp[lane < a.B ? lane : a.B];
+    const int ls = lane < a.B ? lane : a.B - 1;
+    const int32_t lenl = S.len[ls], stl = S.st[ls];
+    const uint64_t below = __builtin_amdgcn_ballot_w64(lane < a.B && int64_t(tpl) * a.Hkv <= x);
+    const int blo = __builtin_popcountll(below) - 1;
+    const int tb0 = __builtin_amdgcn_readlane(tpl, blo);
+    const int nt = __builtin_amdgcn_readlane(tpl, blo + 1) - tb0;
+    const int g = int((x - int64_t(tb0) * a.Hkv) / nt);
+    return {blo, g, nt, int64_t(tb0) * a.Hkv + int64_t(g) * nt, __builtin_amdgcn_readlane(lenl, blo),
+            __builtin_amdgcn_readlane(stl, blo)};
+  }
   // LDS reads land in vector registers; readfirstlane marks the (wave-
   // uniform) values as scalars so the buffer resources built from them stay
   // in SGPRs (otherwise every buffer load becomes a waterfall loop).
