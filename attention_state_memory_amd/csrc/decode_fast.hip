@@ -716,6 +716,19 @@ __device__ __forceinline__ void direct_wave(const DecodeArgs& a, int64_t gw, int
 
 }  // namespace
 
+// Inclusive prefix sum over the 64 lanes of a wave: row shifts by 1, 2, 4
+// and 8 lanes scan each row of 16 (lanes shifted in from outside the row read
+// zero), then each row's total is broadcast to the rows after it.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15 into rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31 into rows 2, 3
+  return x;
+}
+
 // ---------------------------------------------------------------------------
 // One workgroup (block index blk) of the main grid: NW waves.  Eight (two per
 // SIMD) in general; four when every work unit has a wave of its own, so that
@@ -745,33 +758,52 @@ __device__ __forceinline__ void main_block(const DecodeArgs& a, int blk) {
   if (threadIdx.x < NW) ctr[threadIdx.x] = 0;
 
   // tiles per kv head of every sequence, exclusive prefix over sequences
-  int carry = 0;
-  for (int base = 0; base < a.B; base += (NW * 64)) {
-    const int b = base + threadIdx.x;
-    int v = 0;
-    if (b < a.B) {
-      const int n = a.kv_len[b], st = a.kv_start[b];
-      sq_len[b] = n;
-      sq_st[b] = st;
-      const bool valid = n >= 0 && n <= a.max_kv_len && st >= 0 && int64_t(st) + n <= a.kv_capacity;
-      v = valid ? (n + 31) >> 5 : 0;
+  if (a.B < 64) {
+    // one wave scans the lengths with DPP (no LDS round trips) and the
+    // workgroup meets at a single barrier
+    if (w == 0) {
+      int v = 0;
+      if (lane < a.B) {
+        const int n = a.kv_len[lane], st = a.kv_start[lane];
+        sq_len[lane] = n;
+        sq_st[lane] = st;
+        const bool valid = n >= 0 && n <= a.max_kv_len && st >= 0 && int64_t(st) + n <= a.kv_capacity;
+        v = valid ? (n + 31) >> 5 : 0;
+      }
+      const int x = wave_incl_scan(v);
+      if (lane < a.B) tp[lane] = x - v;
+      if (lane == 63) tp[a.B] = x;  // lanes past the last sequence add nothing
     }
-    int x = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(x, o, 64);
-      if (lane >= o) x += y;
-    }
-    if (lane == 63) wsum[w] = x;
     __syncthreads();
-    int before = carry;
-    for (int ww = 0; ww < w; ++ww) before += wsum[ww];
-    if (b < a.B) tp[b] = before + x - v;
-    for (int ww = 0; ww < NW; ++ww) carry += wsum[ww];
+  } else {
+    int carry = 0;
+    for (int base = 0; base < a.B; base += (NW * 64)) {
+      const int b = base + threadIdx.x;
+      int v = 0;
+      if (b < a.B) {
+        const int n = a.kv_len[b], st = a.kv_start[b];
+        sq_len[b] = n;
+        sq_st[b] = st;
+        const bool valid = n >= 0 && n <= a.max_kv_len && st >= 0 && int64_t(st) + n <= a.kv_capacity;
+        v = valid ? (n + 31) >> 5 : 0;
+      }
+      int x = v;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o, 64);
+        if (lane >= o) x += y;
+      }
+      if (lane == 63) wsum[w] = x;
+      __syncthreads();
+      int before = carry;
+      for (int ww = 0; ww < w; ++ww) before += wsum[ww];
+      if (b < a.B) tp[b] = before + x - v;
+      for (int ww = 0; ww < NW; ++ww) carry += wsum[ww];
+      __syncthreads();
+    }
+    if (threadIdx.x == 0) tp[a.B] = carry;
     __syncthreads();
   }
-  if (threadIdx.x == 0) tp[a.B] = carry;
-  __syncthreads();
   if (blk == 0)
     for (int b = threadIdx.x; b <= a.B; b += (NW * 64)) a.tile_prefix[b] = tp[b];
   const int64_t U = int64_t(__builtin_amdgcn_readfirstlane(tp[a.B])) * a.Hkv;
