@@ -787,12 +787,7 @@ __device__ __forceinline__ void main_block(const DecodeArgs& a, int blk) {
         const bool valid = n >= 0 && n <= a.max_kv_len && st >= 0 && int64_t(st) + n <= a.kv_capacity;
         v = valid ? (n + 31) >> 5 : 0;
       }
-      int x = v;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(x, o, 64);
-        if (lane >= o) x += y;
-      }
+      const int x = wave_incl_scan(v);
       if (lane == 63) wsum[w] = x;
       __syncthreads();
       int before = carry;
