@@ -144,14 +144,8 @@ def main():
         run_layers_hier(args)
         return
     if args.workload == "attention_compare":
-        # Switched off: its first run ended with a GPU memory fault reported
-        # after the batch-1 K=1024 step had completed and synchronised; the
-        # faulting kernel is not identified (see the design notes), so the
-        # workload stays off the GPU until a cause is shown.
-        print(json.dumps({"error": "attention_compare is switched off pending a GPU fault "
-                                   "investigation; asm_attend_step itself is covered by "
-                                   "tests/test_gpu_attend.py"}))
-        sys.exit(2)
+        run_compare(args)
+        return
     if args.workload == "batched_decode_whitened":
         run_whitened(args)
         return
@@ -494,14 +488,16 @@ def run_compare(args):
       full attention  asm_attend_step over each sequence's whole context, its
                       own copy of an L-token prefix followed by its local
                       tokens, L in {4096, 8192, 16384};
-      ASM             asm_decode_step with a K-entry memory, K in {1024, 4096,
-                      8192, 16384}, over the local tokens only.
+      ASM             asm_decode_step with a K-entry memory over the local
+                      tokens only: batch 1 at K in {1024, 8192}, batch 32 at
+                      K in {1024, 4096, 8192, 16384}.
     Batch 1 (2048 local tokens) and batch 32 (local lengths uniform in
-    [512, 4096], the headline's seeded replica 0 lengths).  Inputs are seeded
-    draws on the device; enough replicas rotate that a step's working set is
-    not held by the 256 MB last-level cache.  Each configuration is timed as
-    one HIP graph of `steps` calls.  Prints one JSON line with the per-step
-    times and the latency ratio full(L) / ASM(K) for every pair."""
+    [512, 4096], the headline's seeded replica 0 lengths).  Every input is
+    drawn on the timing stream itself, so no step can start before its
+    inputs and workspace exist.  Enough replicas rotate that a step's working
+    set is not held by the 256 MB last-level cache.  Each configuration is
+    timed as one HIP graph of `steps` calls.  Prints one JSON line with the
+    per-step times and the latency ratio full(L) / ASM(K) for every pair."""
     import torch
     from attention_state_memory_amd import api, synth
 
@@ -511,7 +507,10 @@ def run_compare(args):
     Hq, Hkv, d = 32, 8, 128
     scale = synth.softmax_scale(d)
     stream = torch.cuda.Stream(dev)
+    stream.wait_stream(torch.cuda.current_stream(dev))
     steps = max(4, args.steps)
+    asm_K = {1: (1024, 8192), 32: (1024, 4096, 8192, 16384)}
+    Ls = (4096, 8192, 16384)
 
     def normal(shape, seed):
         gen.manual_seed(seed)
@@ -519,79 +518,81 @@ def run_compare(args):
 
     def timed(calls):
         R = len(calls)
-        with torch.cuda.stream(stream):
-            for i in range(R):
-                calls[i]()
+        for i in range(R):
+            calls[i]()
         stream.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=stream):
             for i in range(steps):
                 calls[i % R]()
-        with torch.cuda.stream(stream):
-            g.replay()  # untimed: first replay
+        g.replay()  # untimed: first replay
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        with torch.cuda.stream(stream):
-            e0.record(stream)
-            g.replay()
-            e1.record(stream)
-        torch.cuda.synchronize()
+        stream.synchronize()
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        stream.synchronize()
         return e0.elapsed_time(e1) * 1000.0 / steps
 
     results = {"full_attention_us": {}, "asm_us": {}, "ratio_full_over_asm": {}}
-    for B in (1, 32):
-        lens = [2048] if B == 1 else [int(x) for x in np.random.default_rng([3, 0]).integers(512, 4097, 32)]
-        n_loc = int(sum(lens))
-        kv_start = torch.tensor(np.concatenate([[0], np.cumsum(lens)[:-1]]), dtype=torch.int32, device=dev)
-        kv_len = torch.tensor(lens, dtype=torch.int32, device=dev)
-        q = normal((B, Hq, d), 1)
-        for L in (4096, 8192, 16384):
-            ctx = [L + n for n in lens]
-            ctx_start = torch.tensor(np.concatenate([[0], np.cumsum(ctx)[:-1]]), dtype=torch.int32, device=dev)
-            ctx_len = torch.tensor(ctx, dtype=torch.int32, device=dev)
-            step_bytes = sum(ctx) * Hkv * d * 2 * 2
-            R = max(2, -(-(1 << 30) // step_bytes))  # at least 1 GiB over the replicas
-            reps = [(normal((Hkv, sum(ctx), d), 10 + r), normal((Hkv, sum(ctx), d), 20 + r)) for r in range(R)]
-            out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
-            lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
-            ws = torch.zeros(max(1, api.lib().asm_attend_step_ws(api.BF16, B, Hq, Hkv, d, max(ctx))),
-                             dtype=torch.uint8, device=dev)
+    with torch.cuda.stream(stream):
+        for B in (1, 32):
+            lens = [2048] if B == 1 else [int(x) for x in np.random.default_rng([3, 0]).integers(512, 4097, 32)]
+            n_loc = int(sum(lens))
+            kv_start = torch.tensor(np.concatenate([[0], np.cumsum(lens)[:-1]]), dtype=torch.int32).to(dev)
+            kv_len = torch.tensor(lens, dtype=torch.int32).to(dev)
+            q = normal((B, Hq, d), 1)
+            for L in Ls:
+                print(f"full attention B={B} L={L}: inputs", file=sys.stderr, flush=True)
+                ctx = [L + n for n in lens]
+                ctx_start = torch.tensor(np.concatenate([[0], np.cumsum(ctx)[:-1]]), dtype=torch.int32).to(dev)
+                ctx_len = torch.tensor(ctx, dtype=torch.int32).to(dev)
+                step_bytes = sum(ctx) * Hkv * d * 2 * 2
+                R = max(2, -(-(1 << 30) // step_bytes))  # at least 1 GiB over the replicas
+                reps = [(normal((Hkv, sum(ctx), d), 10 + r), normal((Hkv, sum(ctx), d), 20 + r)) for r in range(R)]
+                out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+                lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+                ws = torch.zeros(max(1, api.lib().asm_attend_step_ws(api.BF16, B, Hq, Hkv, d, max(ctx))),
+                                 dtype=torch.uint8, device=dev)
 
-            def mk(kc, vc):
-                return lambda: api.attend_step(q, kc, vc, ctx_start, ctx_len, max(ctx), scale, out=out,
-                                               out_lse=lse, workspace=ws)
-            us = timed([mk(kc, vc) for kc, vc in reps])
-            results["full_attention_us"][f"B{B}_L{L}"] = us
-            print(f"full attention B={B} L={L}: {us:.1f} us", file=sys.stderr, flush=True)
-            del reps
-        for K in (1024, 4096, 8192, 16384):
-            step_bytes = Hq * K * (d * 2 + 4) + n_loc * Hkv * d * 4
-            R = max(2, -(-(1 << 30) // step_bytes))
-            reps = []
-            for r in range(R):
-                C = normal((Hq, K, d), 100 + r)
-                t = dict(C=C, cinv=api.centroid_inv_norms(C), Abar=normal((Hq, K, d), 200 + r).float(),
-                         LSEbar=torch.full((Hq, K), 8.0, device=dev),
-                         Kl=normal((Hkv, n_loc, d), 300 + r), Vl=normal((Hkv, n_loc, d), 400 + r))
-                reps.append(t)
-            out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
-            lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
-            idx = torch.empty((B, Hq), dtype=torch.int32, device=dev)
-            ws = torch.zeros(api.decode_step_ws(api.BF16, B, Hq, Hkv, d, K, max(lens)),
-                             dtype=torch.uint8, device=dev)
+                def mk(kc, vc):
+                    return lambda: api.attend_step(q, kc, vc, ctx_start, ctx_len, max(ctx), scale, out=out,
+                                                   out_lse=lse, workspace=ws)
+                us = timed([mk(kc, vc) for kc, vc in reps])
+                results["full_attention_us"][f"B{B}_L{L}"] = us
+                print(f"full attention B={B} L={L}: {us:.1f} us", file=sys.stderr, flush=True)
+                del reps
+                stream.synchronize()
+            for K in asm_K[B]:
+                print(f"ASM B={B} K={K}: inputs", file=sys.stderr, flush=True)
+                step_bytes = Hq * K * (d * 2 + 4) + n_loc * Hkv * d * 4
+                R = max(2, -(-(1 << 30) // step_bytes))
+                reps = []
+                for r in range(R):
+                    C = normal((Hq, K, d), 100 + r)
+                    t = dict(C=C, cinv=api.centroid_inv_norms(C), Abar=normal((Hq, K, d), 200 + r).float(),
+                             LSEbar=torch.full((Hq, K), 8.0, device=dev),
+                             Kl=normal((Hkv, n_loc, d), 300 + r), Vl=normal((Hkv, n_loc, d), 400 + r))
+                    reps.append(t)
+                out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+                lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+                idx = torch.empty((B, Hq), dtype=torch.int32, device=dev)
+                ws = torch.zeros(api.decode_step_ws(api.BF16, B, Hq, Hkv, d, K, max(lens)),
+                                 dtype=torch.uint8, device=dev)
 
-            def mk(t):
-                return lambda: api.decode_step(q, t["C"], t["cinv"], t["Abar"], t["LSEbar"], t["Kl"],
-                                               t["Vl"], kv_start, kv_len, max(lens), scale, out=out,
-                                               out_lse=lse, out_idx=idx, workspace=ws)
-            us = timed([mk(t) for t in reps])
-            results["asm_us"][f"B{B}_K{K}"] = us
-            print(f"ASM B={B} K={K}: {us:.1f} us", file=sys.stderr, flush=True)
-            del reps
-        for L in (4096, 8192, 16384):
-            for K in (1024, 4096, 8192, 16384):
-                results["ratio_full_over_asm"][f"B{B}_L{L}_K{K}"] = (
-                    results["full_attention_us"][f"B{B}_L{L}"] / results["asm_us"][f"B{B}_K{K}"])
+                def mk(t):
+                    return lambda: api.decode_step(q, t["C"], t["cinv"], t["Abar"], t["LSEbar"], t["Kl"],
+                                                   t["Vl"], kv_start, kv_len, max(lens), scale, out=out,
+                                                   out_lse=lse, out_idx=idx, workspace=ws)
+                us = timed([mk(t) for t in reps])
+                results["asm_us"][f"B{B}_K{K}"] = us
+                print(f"ASM B={B} K={K}: {us:.1f} us", file=sys.stderr, flush=True)
+                del reps
+                stream.synchronize()
+            for L in Ls:
+                for K in asm_K[B]:
+                    results["ratio_full_over_asm"][f"B{B}_L{L}_K{K}"] = (
+                        results["full_attention_us"][f"B{B}_L{L}"] / results["asm_us"][f"B{B}_K{K}"])
     print(json.dumps({"workload": "attention_compare", "unit": "us per decode step", "steps": steps,
                       "config": {"q_heads": Hq, "kv_heads": Hkv, "head_dim": d, "dtype": "bf16",
                                  "local_len": {"B1": 2048, "B32": "U{512..4096}"},
