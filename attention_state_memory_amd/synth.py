@@ -206,3 +206,13 @@ def mixture_queries(seed, H, N, d, M, sigma=0.3, dtype="bf16") -> np.ndarray:
         out.append(centres[comp] + np.float32(sigma) * _normal(rng, (N, d)))
     X = np.stack(out).astype(np.float32)
     return _store(X, dtype)
+
+
+def device_normal(shape, seed: int, device, dtype=torch.bfloat16):
+    """N(0, 1) draws made on the device by torch's seeded generator (float32,
+    then rounded to `dtype`): for inputs of GB size, where drawing on the host
+    and copying would dominate.  The same seed gives the same bits on every
+    call, so a test can copy any slice back for the oracle."""
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(seed))
+    return torch.randn(tuple(shape), generator=gen, device=device, dtype=torch.float32).to(dtype)
