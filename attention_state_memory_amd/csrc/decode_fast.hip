@@ -731,9 +731,9 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
 
 // ---------------------------------------------------------------------------
 // One workgroup (block index blk) of the main grid: NW waves.  Eight (two per
-// SIMD) in general; four when every work unit has a wave of its own, so that
-// the grid covers twice as many compute units (a workgroup's LDS admits one
-// eight-wave workgroup per compute unit).
+// SIMD) in general; fewer when every work unit has a wave of its own (the
+// direct layout), so that the grid covers more compute units (a workgroup's
+// LDS admits one eight-wave workgroup per compute unit).
 template <int D, int G, int NW>
 __device__ __forceinline__ void main_block(const DecodeArgs& a, int blk) {
   __shared__ int32_t tp[kFastMaxBatch + 1];
@@ -746,10 +746,10 @@ __device__ __forceinline__ void main_block(const DecodeArgs& a, int blk) {
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
   const int64_t gw = int64_t(blk) * NW + w;
-  // The planner takes 4-wave workgroups exactly for the direct layout
-  // (a.direct), so the workgroup size selects it at compile time and the
-  // 8-wave kernel holds none of its code.
-  if constexpr (NW == kSmallWaves) {
+  // The planner takes workgroups of fewer than eight waves exactly for the
+  // direct layout (a.direct), so the workgroup size selects it at compile
+  // time and the 8-wave kernel holds none of its code.
+  if constexpr (NW < kMainWaves) {
     direct_wave<D, G>(a, gw, &ctr[w], vls + w * Tile<D, G>::kVBytes);
     return;
   }
@@ -1011,11 +1011,13 @@ __global__ void __launch_bounds__(256) decode_fast_combine(DecodeArgs a) {
 // the tile prefix, so they load in the first round with the keys; with
 // gathering, so do the units' candidate states, and the winner's state is the
 // candidate of the unit that holds the winning entry.  One dependent round of
-// loads in all (two without gathering: the memory state).
+// loads in all (two without gathering: the memory state).  One wave per
+// workgroup: a step this small has few items, and one wave per compute unit
+// keeps each unit's share of the item loads small.
 template <int G>
-__global__ void __launch_bounds__(256) decode_fast_combine_direct(DecodeArgs a) {
+__global__ void __launch_bounds__(64) decode_fast_combine_direct(DecodeArgs a) {
   const int lane = threadIdx.x & 63;
-  const int item = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int item = blockIdx.x;
   if (item >= a.B * a.Hq) return;
   const int b = item / a.Hq, h = item % a.Hq;
   const int g = h / G, hh = h % G;
@@ -1083,15 +1085,15 @@ template <int D, int G>
 static void launch_fast_hier(const DecodeArgs& a, const HierArgs& h, hipStream_t s) {
   const int lookup_blocks = a.B * a.Hq * h.p;
   if (a.wg_waves == kSmallWaves)
-    hipLaunchKernelGGL((decode_fast_main_hier<D, G, kSmallWaves>),
-                       dim3(unsigned(lookup_blocks + a.n_waves / kSmallWaves)), dim3(kSmallWaves * 64),
+    hipLaunchKernelGGL((decode_fast_main_hier<D, G, kHierSmallWaves>),
+                       dim3(unsigned(lookup_blocks + a.n_waves / kHierSmallWaves)), dim3(kHierSmallWaves * 64),
                        0, s, a, h, lookup_blocks);
   else
     hipLaunchKernelGGL((decode_fast_main_hier<D, G, kMainWaves>),
                        dim3(unsigned(lookup_blocks + a.n_waves / kMainWaves)), dim3(kMainThreads), 0,
                        s, a, h, lookup_blocks);
   if (a.direct)
-    hipLaunchKernelGGL((decode_fast_combine_direct<G>), dim3((a.B * a.Hq + 3) / 4), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((decode_fast_combine_direct<G>), dim3(a.B * a.Hq), dim3(64), 0, s, a);
   else
     hipLaunchKernelGGL((decode_fast_combine<G>), dim3((a.B * a.Hq + 3) / 4), dim3(256), 0, s, a);
 }
@@ -1109,7 +1111,7 @@ static void launch_fast(const DecodeArgs& a, hipStream_t s, int phase = 3) {
   }
   if (phase & 2) {
     if (a.direct)
-      hipLaunchKernelGGL((decode_fast_combine_direct<G>), dim3((a.B * a.Hq + 3) / 4), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((decode_fast_combine_direct<G>), dim3(a.B * a.Hq), dim3(64), 0, s, a);
     else
       hipLaunchKernelGGL((decode_fast_combine<G>), dim3((a.B * a.Hq + 3) / 4), dim3(256), 0, s, a);
   }

@@ -72,6 +72,7 @@ __device__ __forceinline__ uint64_t block_max_u64(uint64_t v, uint64_t* red) {
 // grid).
 template <int D, int NT>
 __device__ __forceinline__ void hier_lookup_block(const HierArgs& a, int blk) {
+  static_assert(NT >= 128 && NT % 64 == 0, "the query load needs a thread per dimension");
   constexpr int kSupersPerThread = hier::supers_per_thread<NT>();
   __shared__ float qs[D];
   __shared__ uint64_t keys_s[kHierMaxSupers];

@@ -67,7 +67,12 @@ struct DecodeArgs {
 constexpr int kFastMaxBatch = 2048;  // sequences per MFMA-path launch
 constexpr int kMainWaves = 8;        // waves per workgroup of the MFMA main grid (two per SIMD)
 constexpr int kMainThreads = 64 * kMainWaves;
-constexpr int kSmallWaves = 4;       // waves per workgroup when the grid has a wave per work unit
+// waves per workgroup when the grid has a wave per work unit (the direct
+// layout): one, so that the grid spreads over as many compute units as it
+// has waves; four in the two-level kernel, whose lookup workgroups share
+// the launch and need at least 128 threads
+constexpr int kSmallWaves = 1;
+constexpr int kHierSmallWaves = 4;
 bool decode_fast_path(int dtype, int d, int G, int K, int64_t kv_tok_stride, int max_kv_len);
 int decode_fast_waves_per_cu(int d, int G);  // resident waves per CU of the MFMA main kernel
 hipError_t launch_decode_fast(const DecodeArgs& a, hipStream_t s);
