@@ -134,9 +134,16 @@ DecodePlan plan_decode(int dtype, int B, int Hq, int Hkv, int d, int K, int max_
     if (w < 2) w = 2;
     w = (w + asmk::kMainWaves - 1) / asmk::kMainWaves * asmk::kMainWaves;
     p.n_waves = int(w);
-    // a wave for every unit (whatever the actual lengths, the roles are then
-    // disjoint): smaller workgroups spread the grid over more compute units
-    p.wg_waves = w >= units ? asmk::kSmallWaves : asmk::kMainWaves;
+    // The direct layout (a wave for every unit, whatever the actual lengths;
+    // one-wave workgroups spread the grid over more compute units) when the
+    // persistent grid is not capped, and also when scoring dominates the
+    // step: local attention waves at most a quarter of the scoring units
+    // (measured at batch 1-4 with K=8192 and batch 2 with K=32768: 8-17%
+    // faster; at half or more the pools win, up to 1.4x at 32 sequences).
+    const int64_t attn_waves = int64_t(Bc) * Hkv *
+        (((int64_t(max_kv_len) + 31) / 32 + kDirectTilesPerWave - 1) / kDirectTilesPerWave);
+    const bool direct = w >= units || 4 * attn_waves <= int64_t(Hq) * score_uph;
+    p.wg_waves = direct ? asmk::kSmallWaves : asmk::kMainWaves;
     // With a wave for every potential unit, tile t of segment s is wave and
     // slot s * mt + t (direct layout: no scan of the lengths); with at most
     // 16 units per head and 8 sequences, the scoring units also gather their
@@ -157,8 +164,10 @@ DecodePlan plan_decode(int dtype, int B, int Hq, int Hkv, int d, int K, int max_
     off = asmk::align_up(off + size_t(Hq) * p.Bc * p.uph * sizeof(uint64_t), kAlign);
     p.off_tp = off;
     off = asmk::align_up(off + size_t(p.Bc + 1) * sizeof(int32_t), kAlign);
-    // one partial state per (rank, segment), two per rank when ranks are wave pairs
-    const size_t pieces = size_t(p.n_waves) + 2 * size_t(p.Bc) * Hkv;
+    // one partial state per (rank, segment), two per rank when ranks are wave
+    // pairs; the direct layout: one per attention wave
+    const size_t pieces = p.direct ? size_t(p.Bc) * Hkv * p.mp
+                                   : size_t(p.n_waves) + 2 * size_t(p.Bc) * Hkv;
     p.off_pa = off;
     off = asmk::align_up(off + pieces * G * d * sizeof(float), kAlign);
     p.off_pl = off;

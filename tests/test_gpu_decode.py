@@ -58,6 +58,26 @@ def test_decode_direct_layout_shapes(case):
     check_decode(inp, out, lse, idx)
 
 
+# Steps too large for a wave per unit at once, but dominated by scoring
+# (local attention waves at most a quarter of the scoring units): the direct
+# layout as well, its grid running in several waves of workgroups; and one
+# step just past that bound, which takes the persistent pools.
+SCORING_DIRECT = [
+    # (seed, d, Hq, Hkv, K, lens)                        what it exercises
+    (26, 128, 32, 8, 8192, [2048]),                       # batch 1 at K=8192: 4352 waves
+    (27, 128, 32, 8, 8192, [2048, 0, 1, 777]),            # 4 sequences, ragged, at the bound
+    (28, 64, 16, 2, 16384, [3000, 45]),                   # d=64, G=8, 256 units per head
+    (29, 128, 32, 8, 8192, [2048] * 5),                   # past the bound: pools
+]
+
+
+@pytest.mark.parametrize("case", SCORING_DIRECT, ids=[f"sd{c[0]}" for c in SCORING_DIRECT])
+def test_decode_scoring_dominated_shapes(case):
+    inp = _case(*case)
+    out, lse, idx = run_decode_gpu(inp)
+    check_decode(inp, out, lse, idx)
+
+
 def test_decode_float32_tiny_shape():
     """One head, d=64, float32, four queries sharing one 32-token local KV."""
     inp = _case(8, 64, 1, 1, 64, [32], dtype="f32")
