@@ -68,6 +68,7 @@ SCORING_DIRECT = [
     (27, 128, 32, 8, 8192, [2048, 0, 1, 777]),            # 4 sequences, ragged, at the bound
     (28, 64, 16, 2, 16384, [3000, 45]),                   # d=64, G=8, 256 units per head
     (29, 128, 32, 8, 8192, [2048] * 5),                   # past the bound: pools
+    (30, 64, 8, 8, 16384, [20] * 39 + [0]),               # 40 sequences (queries in two column tiles), G=1
 ]
 
 
