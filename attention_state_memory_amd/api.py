@@ -79,8 +79,9 @@ SIGNATURES = {
     "asm_decode_step_hier_ws": (_c_size, [_c_int] * 9),
     "asm_decode_step_hier": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                       _c_float, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
-                                      _vp, _vp, _c_i64, _c_i64, _c_i64, _vp, _vp, _c_int,
+                                      _vp, _vp, _vp, _vp, _c_i64, _c_i64, _c_i64, _vp, _vp, _c_int,
                                       _vp, _vp, _vp, _vp, _vp, _c_size, _vp]),
+    "asm_index_group_rows": (_c_int, [_c_int] * 4 + [_vp] * 6),
 }
 
 _lib: Optional[ctypes.CDLL] = None
@@ -563,12 +564,33 @@ def build_index(C, S: int, iters: int, *, workspace=None):
     return SC, scinv, counts, offsets, members
 
 
+def group_index_rows(C, cinv, index):
+    """The entry table grouped by super: (Cg [H, K, d], cginv [H, K]) with
+    row i of head h the entry index[4][h, i] (the members of build_index)."""
+    members = index[4]
+    _dev(C, "C")
+    _dev(cinv, "cinv", torch.float32)
+    _dev(members, "members", torch.int32)
+    code = _dtype_code(C)
+    H, K, d = C.shape
+    Cg = torch.empty_like(C)
+    cginv = torch.empty((H, K), dtype=torch.float32, device=C.device)
+    _check("asm_index_group_rows", lib().asm_index_group_rows(
+        code, H, K, d, _ptr(C), _ptr(cinv), _ptr(members), _ptr(Cg), _ptr(cginv), _stream(C.device)))
+    return Cg, cginv
+
+
 def decode_step_hier(q, C, cinv, index, p: int, Abar, LSEbar, Kl, Vl, kv_start, kv_len,
-                     max_kv_len: int, scale: float, *, out=None, out_lse=None, out_idx=None,
-                     want_probes: bool = False, workspace=None):
+                     max_kv_len: int, scale: float, *, grouped=None, out=None, out_lse=None,
+                     out_idx=None, want_probes: bool = False, workspace=None):
     """Decode step with the two-level lookup.  `index` is the tuple returned
-    by build_index.  Returns (out, out_lse, out_idx, probes | None)."""
+    by build_index; `grouped` (optional) the pair returned by
+    group_index_rows.  Returns (out, out_lse, out_idx, probes | None)."""
     SC, scinv, _, offsets, members = index
+    Cg, cginv = grouped if grouped is not None else (None, None)
+    if Cg is not None:
+        _dev(Cg, "Cg")
+        _dev(cginv, "cginv", torch.float32)
     for t, n in ((q, "q"), (C, "C"), (SC, "SC"), (Kl, "Kl"), (Vl, "Vl")):
         _dev(t, n)
     _dev(cinv, "cinv", torch.float32)
@@ -598,7 +620,8 @@ def decode_step_hier(q, C, cinv, index, p: int, Abar, LSEbar, Kl, Vl, kv_start, 
     ws = _workspace(nbytes, dev, workspace)
     _check("asm_decode_step_hier", lib().asm_decode_step_hier(
         code, B, Hq, Hkv, d, K, S, int(p), float(scale), _ptr(q), _ptr(C), _ptr(cinv), _ptr(SC),
-        _ptr(scinv), _ptr(offsets), _ptr(members), _ptr(Abar), _ptr(LSEbar), _ptr(Kl), _ptr(Vl),
+        _ptr(scinv), _ptr(offsets), _ptr(members), _ptr(Cg), _ptr(cginv), _ptr(Abar), _ptr(LSEbar),
+        _ptr(Kl), _ptr(Vl),
         Kl.stride(0), Kl.stride(1), cap, _ptr(kv_start), _ptr(kv_len), int(max_kv_len), _ptr(out),
         _ptr(out_lse), _ptr(out_idx), _ptr(probes), _ptr(ws), nbytes, _stream(dev)))
     return out, out_lse, out_idx, probes

@@ -575,7 +575,8 @@ size_t asm_decode_step_hier_ws(int dtype, int B, int Hq, int Hkv, int d, int K, 
 int asm_decode_step_hier(int dtype, int B, int Hq, int Hkv, int d, int K, int S, int p,
                          float scale, const void* q, const void* C, const float* cinv,
                          const void* SC, const float* scinv, const int32_t* offsets,
-                         const int32_t* members, const float* Abar, const float* LSEbar,
+                         const int32_t* members, const void* Cg, const float* cginv,
+                         const float* Abar, const float* LSEbar,
                          const void* Kl, const void* Vl, int64_t kv_head_stride,
                          int64_t kv_tok_stride, int64_t kv_capacity, const int32_t* kv_start,
                          const int32_t* kv_len, int max_kv_len, float* out, float* out_lse,
@@ -591,10 +592,13 @@ int asm_decode_step_hier(int dtype, int B, int Hq, int Hkv, int d, int K, int S,
   if (int64_t(K) * d * 2 >= (int64_t(1) << 31))
     return fail(ASM_ERR_SHAPE, "one head's entry table must stay under 2 GiB (K=%d)", K);
   if (!SC || !scinv || !offsets || !members) return fail(ASM_ERR_NULL, "SC, scinv, offsets and members are required");
-  ASM_TRY(check_bf16_ptrs(dtype, {SC}));
+  if ((Cg == nullptr) != (cginv == nullptr))
+    return fail(ASM_ERR_NULL, "Cg and cginv must both be given or both be NULL");
+  ASM_TRY(check_bf16_ptrs(dtype, {SC, Cg}));
   asmk::HierArgs h{};
   h.Hq = Hq; h.K = K; h.S = S; h.d = d; h.p = p;
   h.C = C; h.cinv = cinv; h.SC = SC; h.scinv = scinv; h.offsets = offsets; h.members = members;
+  h.Cg = Cg; h.cginv = cginv;
   h.probes_out = out_probes;
   return decode_impl(dtype, B, Hq, Hkv, d, K, scale, q, C, cinv, Abar, LSEbar, Kl, Vl,
                      kv_head_stride, kv_tok_stride, kv_capacity, kv_start, kv_len, max_kv_len,
@@ -857,6 +861,23 @@ static size_t build_index_ws_bytes(int H, int K, int S) {
   size_t off = asmk::align_up(size_t(H) * K * sizeof(int32_t), kAlign);  // entry -> super
   off += asmk::align_up(size_t(H) * S * sizeof(int32_t), kAlign);        // scatter cursors
   return off;
+}
+
+int asm_index_group_rows(int dtype, int H, int K, int d, const void* C, const float* cinv,
+                         const int32_t* members, void* Cg, float* cginv, hipStream_t stream) {
+  ASM_TRY(check_dtype(dtype));
+  if (d != 64 && d != 128) return fail(ASM_ERR_SHAPE, "need d in {64, 128} (d=%d)", d);
+  if (H < 1 || K < 1) return fail(ASM_ERR_SHAPE, "need H, K >= 1 (H=%d, K=%d)", H, K);
+  if (!C || !cinv || !members || !Cg || !cginv)
+    return fail(ASM_ERR_NULL, "C, cinv, members, Cg and cginv are required");
+  if (!aligned16(C) || !aligned16(Cg)) return fail(ASM_ERR_ALIGN, "C and Cg must be 16-byte aligned");
+  const size_t row_bytes = size_t(d) * (dtype == ASM_BF16 ? 2 : 4);
+  const char* c0 = static_cast<const char*>(C);
+  const char* g0 = static_cast<const char*>(Cg);
+  const size_t bytes = size_t(H) * K * row_bytes;
+  if (g0 < c0 + bytes && c0 < g0 + bytes) return fail(ASM_ERR_SHAPE, "Cg must not overlap C");
+  return hip_status(asmk::launch_index_group_rows(dtype, H, K, d, C, cinv, members, Cg, cginv, stream),
+                    "index_group_rows");
 }
 
 size_t asm_build_index_ws(int dtype, int H, int K, int S, int d) {

@@ -20,7 +20,10 @@
 //      carry the index, lowest index first on exact score ties);
 //   4. the probe's members are scored and the block-wide maximum key, the
 //      member of highest score and lowest index, is written as unit r of
-//      (head, sequence) where the flat search writes its unit keys.  The
+//      (head, sequence) where the flat search writes its unit keys; with the
+//      table grouped by super (Cg, cginv), the member rows sit at the
+//      probe's member positions, so they load in the same round as the
+//      member indices instead of after them.  The
 //      flat path's merge kernel reduces the p units to the entry, and its
 //      attention kernel runs unchanged with scoring switched off.
 #pragma once
@@ -116,11 +119,19 @@ __device__ __forceinline__ void hier_lookup_block(const HierArgs& a, int blk) {
   if (probe >= 0) {
     const uint16_t* C = static_cast<const uint16_t*>(a.C) + size_t(h) * a.K * D;
     const float* cinv = a.cinv + size_t(h) * a.K;
-    const int32_t* mem = a.members + size_t(h) * a.K + off[probe];
-    const int n = off[probe + 1] - off[probe];
-    for (int j = t; j < n; j += NT) {
-      const int e = mem[j];
-      best = umax64(best, argmax_key(hier::dot_row<D>(C + size_t(e) * D, qs) * cinv[e], uint32_t(e)));
+    const int o0 = off[probe];
+    const int32_t* mem = a.members + size_t(h) * a.K + o0;
+    const int n = off[probe + 1] - o0;
+    if (a.Cg != nullptr) {
+      const uint16_t* Cg = static_cast<const uint16_t*>(a.Cg) + (size_t(h) * a.K + o0) * D;
+      const float* cg = a.cginv + size_t(h) * a.K + o0;
+      for (int j = t; j < n; j += NT)
+        best = umax64(best, argmax_key(hier::dot_row<D>(Cg + size_t(j) * D, qs) * cg[j], uint32_t(mem[j])));
+    } else {
+      for (int j = t; j < n; j += NT) {
+        const int e = mem[j];
+        best = umax64(best, argmax_key(hier::dot_row<D>(C + size_t(e) * D, qs) * cinv[e], uint32_t(e)));
+      }
     }
   }
   best = hier::block_max_u64<NT>(best, red);

@@ -95,10 +95,16 @@ struct HierArgs {
   const float* scinv;   // [Hq, S]
   const int32_t* offsets;  // [Hq, S + 1]
   const int32_t* members;  // [Hq, K]
+  const void* Cg;       // [Hq, K, d] nullable: C[h, members[h, i]] at row i (grouped by super)
+  const float* cginv;   // [Hq, K] nullable: cinv in the same order
   uint64_t* keys;       // [Hq, B, p] one argmax key per (head, sequence, probe)
   int32_t* probes_out;  // [B, Hq, p] nullable
 };
 bool hier_fast_path(int dtype, int d);
+// Cg[h, i] = C[h, members[h, i]], cginv[h, i] = cinv[h, members[h, i]] (a
+// zero row and 0 for a member outside [0, K))
+hipError_t launch_index_group_rows(int dtype, int H, int K, int d, const void* C, const float* cinv,
+                                   const int32_t* members, void* Cg, float* cginv, hipStream_t s);
 // the main grid with the lookup fused in (MFMA path only), then the combine
 hipError_t launch_decode_hier(const DecodeArgs& a, const HierArgs& h, hipStream_t s);
 

@@ -465,6 +465,45 @@ __global__ void __launch_bounds__(256) agg_finalize_bf16(AggregateArgs a) {
   if (sub == 0) a.LSEbar[it] = float(double(mx) + log(z) - log(double(n)));
 }
 
+// ---------------------------------------------------------------------------
+// the entry table grouped by super (two-level index): row i of head h is
+// entry members[h, i], copied 16 bytes per thread; cginv follows
+// ---------------------------------------------------------------------------
+template <int ES>  // element size in bytes
+__global__ void __launch_bounds__(256) index_group_rows_kernel(int H, int K, int d, const char* C,
+                                                               const float* cinv, const int32_t* members,
+                                                               char* Cg, float* cginv) {
+  const int pieces = d * ES / 16;  // d * ES is a multiple of 16
+  const int64_t total = int64_t(H) * K * pieces;
+  for (int64_t x = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; x < total;
+       x += int64_t(gridDim.x) * blockDim.x) {
+    const int64_t row = x / pieces;
+    const int part = int(x - row * pieces);
+    const int64_t h = row / K;
+    const int e = members[row];
+    const bool ok = e >= 0 && e < K;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (ok) v = *reinterpret_cast<const u32x4*>(C + (h * K + e) * d * ES + part * 16);
+    *reinterpret_cast<u32x4*>(Cg + row * d * ES + part * 16) = v;
+    if (part == 0) cginv[row] = ok ? cinv[h * K + e] : 0.0f;
+  }
+}
+
+hipError_t launch_index_group_rows(int dtype, int H, int K, int d, const void* C, const float* cinv,
+                                   const int32_t* members, void* Cg, float* cginv, hipStream_t s) {
+  const int es = dtype == 0 ? 2 : 4;
+  const int64_t total = int64_t(H) * K * (d * es / 16);
+  if (total == 0) return hipSuccess;
+  const dim3 grid(unsigned((total + 255) / 256 < 65536 ? (total + 255) / 256 : 65536));
+  if (es == 2)
+    hipLaunchKernelGGL(index_group_rows_kernel<2>, grid, dim3(256), 0, s, H, K, d,
+                       static_cast<const char*>(C), cinv, members, static_cast<char*>(Cg), cginv);
+  else
+    hipLaunchKernelGGL(index_group_rows_kernel<4>, grid, dim3(256), 0, s, H, K, d,
+                       static_cast<const char*>(C), cinv, members, static_cast<char*>(Cg), cginv);
+  return hipGetLastError();
+}
+
 hipError_t launch_aggregate(const AggregateArgs& a, int dtype, hipStream_t s) {
   const int64_t HK = int64_t(a.H) * a.K, HN = int64_t(a.H) * a.N;
   if (HK == 0) return hipSuccess;

@@ -702,8 +702,10 @@ def run_layers_hier(args):
     query head (8192), once with the flat search and once with the two-level
     lookup (`--supers` S = 128, `--probes` p = 8).  The entries are clusterable (64-centre mixture
     queries per head, as a built memory's are) and every layer's query is an
-    entry plus noise.  Reports per-layer time of both lookups and the
-    two-level lookup's recall@1 against the flat search."""
+    entry plus noise.  The two-level lookup reads the entry table grouped by
+    super (asm_index_group_rows); it is also timed through the member list.
+    Reports per-layer time of the lookups and the two-level lookup's
+    recall@1 against the flat search."""
     import torch
     from attention_state_memory_amd import api, synth
 
@@ -730,6 +732,7 @@ def run_layers_hier(args):
         t["C"] = to_dev(C)
         t["cinv"] = api.centroid_inv_norms(t["C"])
         t["index"] = api.build_index(t["C"], S, 4)
+        t["grouped"] = api.group_index_rows(t["C"], t["cinv"], t["index"])
         L.append(t)
         print(f"layer {l} resident", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
@@ -750,10 +753,11 @@ def run_layers_hier(args):
                         t["kv_start"], t["kv_len"], 2048, scale, out=out[l], out_lse=lse[l],
                         out_idx=idx_f[l], workspace=ws)
 
-    def hier(l):
+    def hier(l, grouped=True):
         t = L[l]
         api.decode_step_hier(t["q"], t["C"], t["cinv"], t["index"], p, t["Abar"], t["LSEbar"],
                              t["Kl"], t["Vl"], t["kv_start"], t["kv_len"], 2048, scale,
+                             grouped=t["grouped"] if grouped else None,
                              out=out[l], out_lse=lse[l], out_idx=idx_h[l], workspace=ws)
 
     def timed(fn):
@@ -780,6 +784,7 @@ def run_layers_hier(args):
         return e0.elapsed_time(e1) / reps, reps
 
     ms_flat, _ = timed(flat)
+    ms_members, _ = timed(lambda l: hier(l, grouped=False))
     ms_hier, reps = timed(hier)
     recall = float((idx_f == idx_h).float().mean().item())
     rows = p * K / S  # member rows scanned per query head on average
@@ -798,6 +803,7 @@ def run_layers_hier(args):
                    "probes": p, "batch": 1, "q_heads": Hq, "kv_heads": 8, "head_dim": 128,
                    "local_len": 2048, "launch": "hip_graph"},
         "flat_us_per_layer": ms_flat * 1e3 / layers,
+        "through_member_list_us_per_layer": ms_members * 1e3 / layers,
         "speedup_vs_flat": ms_flat / ms_hier,
         "recall_at_1_vs_flat": recall,
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",

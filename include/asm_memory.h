@@ -64,7 +64,7 @@ enum asm_status_code {
 enum asm_dtype { ASM_BF16 = 0, ASM_F32 = 1 };
 
 /* ABI version of this header (bumped on any signature change). */
-#define ASM_ABI_VERSION 8
+#define ASM_ABI_VERSION 9
 int asm_abi_version(void);
 
 /* Static text for a status code. */
@@ -234,6 +234,11 @@ int asm_attend_step(int dtype, int B, int Hq, int Hkv, int d, float scale, const
  *   1 <= p <= 32.
  *   SC [Hq, S, d] bf16; scinv [Hq, S]; offsets [Hq, S+1]; members [Hq, K]
  *   int32: as written by asm_build_index.
+ *   Cg [Hq, K, d] bf16 and cginv [Hq, K] (both NULL, or both given): the
+ *   entry table grouped by super, as written by asm_index_group_rows from
+ *   C, cinv and members.  Given, the probed members' rows are read from Cg
+ *   at their member positions, one dependent load round fewer than through
+ *   members into C; the results are the same.
  *   out_probes [B, Hq, p] int32 (nullable): the probed supers, best first,
  *   -1 past the number of non-empty supers.  The probes of rank p-1 and
  *   below that tie exactly in score resolve to the lower super index.
@@ -245,7 +250,8 @@ size_t asm_decode_step_hier_ws(int dtype, int B, int Hq, int Hkv, int d, int K, 
 int asm_decode_step_hier(int dtype, int B, int Hq, int Hkv, int d, int K, int S, int p,
                          float scale, const void* q, const void* C, const float* cinv,
                          const void* SC, const float* scinv, const int32_t* offsets,
-                         const int32_t* members, const float* Abar, const float* LSEbar,
+                         const int32_t* members, const void* Cg, const float* cginv,
+                         const float* Abar, const float* LSEbar,
                          const void* Kl, const void* Vl, int64_t kv_head_stride,
                          int64_t kv_tok_stride, int64_t kv_capacity, const int32_t* kv_start,
                          const int32_t* kv_len, int max_kv_len, float* out, float* out_lse,
@@ -433,6 +439,20 @@ size_t asm_build_index_ws(int dtype, int H, int K, int S, int d);
 int asm_build_index(int dtype, int H, int K, int S, int d, int iters, const void* C, void* SC,
                     float* scinv, int32_t* counts, int32_t* offsets, int32_t* members, void* ws,
                     size_t ws_bytes, hipStream_t stream);
+
+/*
+ * asm_index_group_rows -- the entry table grouped by super, for
+ * asm_decode_step_hier ([TS] Complejidad: the members of a probed super are
+ * then contiguous).  Cg[h, i, :] = C[h, members[h, i], :] and
+ * cginv[h, i] = cinv[h, members[h, i]] for every head h and i < K; a member
+ * outside [0, K) gives a zero row and 0.  Rebuild it whenever C, cinv or
+ * the index change.
+ *   dtype bf16 or float32; d in {64, 128}; C, Cg [H, K, d] 16-byte aligned,
+ *   not overlapping; cinv, cginv [H, K] float32; members [H, K] int32.
+ *   No workspace.
+ */
+int asm_index_group_rows(int dtype, int H, int K, int d, const void* C, const float* cinv,
+                         const int32_t* members, void* Cg, float* cginv, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -41,9 +41,9 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_text():
     L = api.lib()
-    assert L.asm_abi_version() == 8
+    assert L.asm_abi_version() == 9
     text = open(HEADER).read()
-    assert int(re.search(r"#define ASM_ABI_VERSION (\d+)", text).group(1)) == 8
+    assert int(re.search(r"#define ASM_ABI_VERSION (\d+)", text).group(1)) == 9
     assert L.asm_status_str(0) == b"ok"
     assert L.asm_status_str(-5).startswith(b"workspace")
 
@@ -256,3 +256,20 @@ def test_header_compiles_and_links_as_c(tmp_path):
     r = subprocess.run([str(exe)], capture_output=True, text=True)
     assert r.returncode == 0, (r.returncode, r.stdout, r.stderr)
     assert r.stdout.strip() == f"{len(names)} entry points"
+
+
+def test_index_group_rows_validation_before_any_launch():
+    """asm_index_group_rows refuses a bad dtype, head dim, count, null
+    pointer, misalignment or an output overlapping the table, before any
+    device call."""
+    L = api.lib()
+
+    def call(dtype=0, H=2, K=8, d=128, C=1 << 20, cinv=1 << 22, mem=1 << 23, Cg=1 << 24, cg=1 << 25):
+        return L.asm_index_group_rows(dtype, H, K, d, C, cinv, mem, Cg, cg, None)
+    assert call(dtype=7) == -3
+    assert call(d=96) == -2
+    assert call(K=0) == -2 and call(H=0) == -2
+    assert call(C=NULL) == -1 and call(mem=NULL) == -1 and call(cg=NULL) == -1
+    assert call(C=(1 << 20) + 8) == -4 and call(Cg=(1 << 24) + 8) == -4
+    assert call(Cg=(1 << 20) + 2 * 8 * 128) == -2       # bf16 [2, 8, 128] = 4 KiB from C: overlaps
+    assert b"overlap" in L.asm_last_error()

@@ -87,14 +87,15 @@ def _hier_case(seed, B, Hq, Hkv, K, S, lens, M=48):
     return inp
 
 
-def _run_hier(inp, S, p, iters=4):
+def _run_hier(inp, S, p, iters=4, grouped=False):
     C = dev(inp["C"])
     cinv = api.centroid_inv_norms(C)
     index = api.build_index(C, S, iters)
+    g = api.group_index_rows(C, cinv, index) if grouped else None
     out, lse, idx, probes = api.decode_step_hier(
         dev(inp["q"]), C, cinv, index, p, dev(inp["Abar"]), dev(inp["LSEbar"]), dev(inp["Kl"]),
         dev(inp["Vl"]), dev(inp["kv_start"]), dev(inp["kv_len"]), int(np.max(inp["kv_len"])),
-        inp["scale"], want_probes=True)
+        inp["scale"], grouped=g, want_probes=True)
     torch.cuda.synchronize()
     return [host(x) for x in index], host(out), host(lse), host(idx), host(probes)
 
@@ -197,3 +198,61 @@ def test_decode_hier_more_probes_than_supers():
     ref, ref_lse = O.decode_with_idx(q64, idx, widen(inp["Abar"]), widen(inp["LSEbar"]), ks, vs,
                                      inp["scale"])
     assert_states_close(out, lse, ref, ref_lse)
+
+
+def test_index_group_rows_matches_indexing():
+    """asm_index_group_rows is a row gather: Cg[h, i] = C[h, members[h, i]],
+    cginv likewise; a member outside [0, K) gives a zero row and 0."""
+    H, K, d = 3, 700, 128
+    C = synth.mixture_queries([405, 0], H, K, d, M=8, dtype="bf16")
+    r = np.random.default_rng([405, 1])
+    members = np.stack([r.permutation(K) for _ in range(H)]).astype(np.int32)
+    members[1, 5], members[2, 0] = -1, K
+    Ct = dev(C)
+    cinv = api.centroid_inv_norms(Ct)
+    index = (None, None, None, None, dev(members))
+    Cg, cg = api.group_index_rows(Ct, cinv, index)
+    torch.cuda.synchronize()
+    Cg, cg, ci = host(Cg), host(cg), host(cinv)
+    for h in range(H):
+        ok = (members[h] >= 0) & (members[h] < K)
+        np.testing.assert_array_equal(Cg[h][ok], C[h][members[h][ok]])
+        np.testing.assert_array_equal(cg[h][ok], ci[h][members[h][ok]])
+        assert np.all(Cg[h][~ok] == 0) and np.all(cg[h][~ok] == 0)
+
+
+@pytest.mark.parametrize("case", ["small", "beyond_resident"])
+def test_decode_hier_grouped_table_is_identical(case):
+    """With the table grouped by super the two-level step reads the same
+    rows in another order: indices, probes and outputs are bit-identical to
+    the step through the member list, and follow the oracle."""
+    if case == "small":
+        inp = _hier_case(1, B=6, Hq=16, Hkv=4, K=2048, S=48, lens=[300, 0, 17, 1024, 64, 33])
+        S, p, iters = 48, 4, 4
+    else:
+        lens = np.random.default_rng([404, 0]).integers(0, 300, 40).tolist()
+        inp = _hier_case(5, B=40, Hq=32, Hkv=8, K=2048, S=64, lens=lens)
+        S, p, iters = 64, 8, 2
+    # one index (its member order within a super is unspecified), two lookups
+    C = dev(inp["C"])
+    cinv = api.centroid_inv_norms(C)
+    index_t = api.build_index(C, S, iters)
+    res = []
+    for g in (None, api.group_index_rows(C, cinv, index_t)):
+        r = api.decode_step_hier(
+            dev(inp["q"]), C, cinv, index_t, p, dev(inp["Abar"]), dev(inp["LSEbar"]), dev(inp["Kl"]),
+            dev(inp["Vl"]), dev(inp["kv_start"]), dev(inp["kv_len"]), int(np.max(inp["kv_len"])),
+            inp["scale"], grouped=g, want_probes=True)
+        torch.cuda.synchronize()
+        res.append([host(x) for x in r])
+    (out, lse, idx, probes), (out_g, lse_g, idx_g, probes_g) = res
+    index_g = [host(x) for x in index_t]
+    np.testing.assert_array_equal(idx_g, idx)
+    np.testing.assert_array_equal(probes_g, probes)
+    if case == "small":  # a wave per unit: bit-identical run to run
+        np.testing.assert_array_equal(out_g, out)
+        np.testing.assert_array_equal(lse_g, lse)
+    else:  # the pools' split of the local tiles is decided at run time: last bits only
+        np.testing.assert_allclose(out_g, out, rtol=0, atol=1e-6)
+        np.testing.assert_allclose(lse_g, lse, rtol=0, atol=1e-6)
+    _check_hier(inp, index_g, idx_g, probes_g, p)
