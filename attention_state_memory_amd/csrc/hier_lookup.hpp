@@ -39,12 +39,9 @@ namespace hier {
 template <int NT>
 constexpr int supers_per_thread() { return (kHierMaxSupers + NT - 1) / NT; }
 
-// q . row over D bf16 values, the query in LDS as float32
+// q . row over D bf16 values held in registers, the query in LDS as float32
 template <int D>
-__device__ __forceinline__ float dot_row(const uint16_t* row, const float* qs) {
-  u32x4 v[D / 8];
-#pragma unroll
-  for (int c = 0; c < D / 8; ++c) v[c] = ld16(row + 8 * c);
+__device__ __forceinline__ float dot_regs(const u32x4 (&v)[D / 8], const float* qs) {
   float acc = 0.0f;
 #pragma unroll
   for (int c = 0; c < D / 8; ++c)
@@ -54,6 +51,15 @@ __device__ __forceinline__ float dot_row(const uint16_t* row, const float* qs) {
       acc = fmaf(bf16_hi(v[c][e]), qs[8 * c + 2 * e + 1], acc);
     }
   return acc;
+}
+
+// q . row over D bf16 values in memory
+template <int D>
+__device__ __forceinline__ float dot_row(const uint16_t* row, const float* qs) {
+  u32x4 v[D / 8];
+#pragma unroll
+  for (int c = 0; c < D / 8; ++c) v[c] = ld16(row + 8 * c);
+  return dot_regs<D>(v, qs);
 }
 
 // block-wide maximum of one key per thread (all NT threads take part)
@@ -86,21 +92,36 @@ __device__ __forceinline__ void hier_lookup_block(const HierArgs& a, int blk) {
   const int item = blk / a.p;     // b * Hq + h
   const int b = item / a.Hq, h = item % a.Hq;
 
+  const uint16_t* SC = static_cast<const uint16_t*>(a.SC) + size_t(h) * a.S * D;
+  const float* scinv = a.scinv + size_t(h) * a.S;
+  const int32_t* off = a.offsets + size_t(h) * (a.S + 1);
+  // The thread's first super (its row, inverse norm and member range) does
+  // not depend on the query: it loads beside the query, in the same round.
+  u32x4 row0[D / 8];
+  float si0 = 0.0f;
+  int ob0 = 0, oe0 = 0;
+  if (t < a.S) {
+#pragma unroll
+    for (int c = 0; c < D / 8; ++c) row0[c] = ld16(SC + size_t(t) * D + 8 * c);
+    si0 = scinv[t];
+    ob0 = off[t];
+    oe0 = off[t + 1];
+  }
   const uint16_t* qp = static_cast<const uint16_t*>(a.q) + size_t(item) * D;
   if (t < D) qs[t] = load_elem(qp, t);
   if (t == 0) probe_s = -1;
   __syncthreads();
 
-  const uint16_t* SC = static_cast<const uint16_t*>(a.SC) + size_t(h) * a.S * D;
-  const float* scinv = a.scinv + size_t(h) * a.S;
-  const int32_t* off = a.offsets + size_t(h) * (a.S + 1);
   uint64_t sk[kSupersPerThread];
 #pragma unroll
   for (int i = 0; i < kSupersPerThread; ++i) {
     const int s = t + NT * i;
     sk[i] = 0ull;
-    if (s < a.S && off[s + 1] > off[s])
+    if (i == 0) {
+      if (s < a.S && oe0 > ob0) sk[0] = argmax_key(hier::dot_regs<D>(row0, qs) * si0, uint32_t(s));
+    } else if (s < a.S && off[s + 1] > off[s]) {
       sk[i] = argmax_key(hier::dot_row<D>(SC + size_t(s) * D, qs) * scinv[s], uint32_t(s));
+    }
     if (s < a.S) keys_s[s] = sk[i];
   }
   __syncthreads();
