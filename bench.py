@@ -74,7 +74,8 @@ def measured_traffic(profile_name: str, sources) -> dict:
 # the decode kernels' sources: a change to any of them voids the counters
 DECODE_SOURCES = ("attention_state_memory_amd/csrc/decode_fast.hip",
                   "attention_state_memory_amd/csrc/common.hpp",
-                  "attention_state_memory_amd/csrc/kernels.hpp")
+                  "attention_state_memory_amd/csrc/kernels.hpp",
+                  "attention_state_memory_amd/csrc/hier_lookup.hpp")
 
 
 def algorithmic_bytes_split(inp):
