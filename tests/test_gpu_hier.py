@@ -256,3 +256,19 @@ def test_decode_hier_grouped_table_is_identical(case):
         np.testing.assert_allclose(out_g, out, rtol=0, atol=1e-6)
         np.testing.assert_allclose(lse_g, lse, rtol=0, atol=1e-6)
     _check_hier(inp, index_g, idx_g, probes_g, p)
+
+
+def test_index_group_rows_float32():
+    """The row gather on a float32 table (d=64): the same indexing."""
+    H, K, d = 2, 333, 64
+    r = np.random.default_rng([405, 2])
+    C = r.standard_normal((H, K, d)).astype(np.float32)
+    members = np.stack([r.permutation(K) for _ in range(H)]).astype(np.int32)
+    Ct = dev(C)
+    cinv = api.centroid_inv_norms(Ct)
+    Cg, cg = api.group_index_rows(Ct, cinv, (None, None, None, None, dev(members)))
+    torch.cuda.synchronize()
+    Cg, cg, ci = host(Cg), host(cg), host(cinv)
+    for h in range(H):
+        np.testing.assert_array_equal(Cg[h], C[h][members[h]])
+        np.testing.assert_array_equal(cg[h], ci[h][members[h]])

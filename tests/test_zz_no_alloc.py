@@ -71,6 +71,10 @@ def _assert_identical(got, want, what):
 STEPS = [
     # the batched step (32 sequences, K=8192, lengths uniform in [512, 4096])
     ("batched K8192", lambda: synth.batched_decode(0)),
+    # one sequence at K=8192: scoring dominates, so the direct layout runs
+    # in several waves of one-wave workgroups
+    ("batch-1 K8192", lambda: synth.decode_inputs([240, 3], B=1, Hq=32, Hkv=8, d=128, K=8192,
+                                                  kv_lens=[2048])),
     # smaller: an empty and a ragged sequence, K=512
     ("small ragged", lambda: synth.decode_inputs([240, 1], B=3, Hq=32, Hkv=8, d=128, K=512,
                                                  kv_lens=[0, 70, 513])),
