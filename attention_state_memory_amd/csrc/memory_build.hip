@@ -361,25 +361,34 @@ __global__ void __launch_bounds__(256) agg_finalize_bf16(AggregateArgs a) {
   double c[8];
   if (n > 0) {
     double sum[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
-    for (int m0 = 0; m0 < n; m0 += LG) {
-      const int cnt = min(LG, n - m0);
-      const int myi = sub < cnt ? mem[m0 + sub] : 0;
-      for (int b0 = 0; b0 < cnt; b0 += XB) {
-        u32x4 v[XB];
+    for (int M0 = 0; M0 < n; M0 += 4 * LG) {
+      // the member indices of up to four chunks of LG members load in one
+      // round; lane `sub` holds member M0 + c*LG + sub of chunk c
+      int ids[4];
 #pragma unroll
-        for (int j = 0; j < XB; ++j) {
-          const int mm = b0 + j;
-          const int row = __shfl(myi, g0 + (mm & (LG - 1)), 64);
-          // members past cnt read from past the buffer end: zeros, no traffic
-          v[j] = buf16(rx, mm < cnt ? (row * D + 8 * sub) * 2 : x_oob, 0);
-        }
+      for (int c = 0; c < 4; ++c) ids[c] = M0 + c * LG + sub < n ? mem[M0 + c * LG + sub] : 0;
 #pragma unroll
-        for (int j = 0; j < XB; ++j)
+      for (int c = 0; c < 4; ++c) {
+        const int m0 = M0 + c * LG;
+        if (m0 >= n) break;
+        const int cnt = min(LG, n - m0);
+        for (int b0 = 0; b0 < cnt; b0 += XB) {
+          u32x4 v[XB];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            sum[2 * e] += double(bf16_lo(v[j][e]));
-            sum[2 * e + 1] += double(bf16_hi(v[j][e]));
+          for (int j = 0; j < XB; ++j) {
+            const int mm = b0 + j;
+            const int row = __shfl(ids[c], g0 + (mm & (LG - 1)), 64);
+            // members past cnt read from past the buffer end: zeros, no traffic
+            v[j] = buf16(rx, mm < cnt ? (row * D + 8 * sub) * 2 : x_oob, 0);
           }
+#pragma unroll
+          for (int j = 0; j < XB; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              sum[2 * e] += double(bf16_lo(v[j][e]));
+              sum[2 * e + 1] += double(bf16_hi(v[j][e]));
+            }
+        }
       }
     }
     u32x4 packed;
